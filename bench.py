@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of libeuler_attn: one step = the whole causal-GQA-attention hot path on one
+batch of seeded synthetic inputs already resident in HBM:
+
+    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, main, dQ finalize) -> RoPE^-1(dQ), RoPE^-1(dK)
+
+Throughput is reported as TFLOP/s at the exact causal FLOP count 14 * D * B * Hq * T(T+1)/2
+(4D forward + 10D backward per unmasked query/key pair) and as a fraction of the MI355X
+dense bf16 MFMA peak.  Default workload: batch 4, T = 1024, 12 query / 4 KV heads,
+head_dim 64, bf16 I/O (the blog's benchmark shape).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--extra NAMES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA attention fwd+bwd TFLOP/s and % of MFMA peak (T=1024, 12Q/4KV, d=64)"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (256 CU x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "attn_fwd": ["causal_gqa_attention_fwd_amd/csrc/attn_fwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_bwd_main": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Step:
+    """Preallocated buffers and the eight launches of one step, called through the C ABI."""
+
+    def __init__(self, w, inp, torch, ea):
+        self.w = w
+        dev = torch.device("cuda", 0)
+        self.q_raw = inp["q_raw"].to(dev)
+        self.k_raw = inp["k_raw"].to(dev)
+        self.v = inp["v"].to(dev)
+        self.do = inp["dout"].to(dev)
+        self.qr = torch.empty_like(self.q_raw)
+        self.kr = torch.empty_like(self.k_raw)
+        self.o = torch.empty_like(self.q_raw)
+        self.lse = torch.empty((w.B, w.Hq, w.T), device=dev, dtype=torch.float32)
+        self.dq = torch.empty_like(self.q_raw)
+        self.dk = torch.empty_like(self.k_raw)
+        self.dv = torch.empty_like(self.v)
+        self.dq_raw = torch.empty_like(self.q_raw)
+        self.dk_raw = torch.empty_like(self.k_raw)
+        dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+        nws = ea.attn_bwd_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, self.q_raw.dtype)
+        self.ws = torch.empty(nws, device=dev, dtype=torch.uint8)
+        L = ea.lib()
+        scale = 1.0 / (w.D ** 0.5)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        B, T, Hq, Hkv, D, base = w.B, w.T, w.Hq, w.Hkv, w.D, w.base
+        p = lambda t: t.data_ptr()  # noqa: E731
+        # (name, ctypes function, arguments) for each launch, in order.
+        self.calls = [
+            ("rope_q", L.rope_apply, (p(self.q_raw), p(self.qr), B, T, Hq, D, dtc, base, 0, 0, stream)),
+            ("rope_k", L.rope_apply, (p(self.k_raw), p(self.kr), B, T, Hkv, D, dtc, base, 0, 0, stream)),
+            ("attn_fwd", L.attn_fwd, (p(self.qr), p(self.kr), p(self.v), p(self.o), p(self.lse), B, T, Hq,
+                                      Hkv, D, scale, dtc, stream)),
+            ("attn_bwd_pre", L.attn_bwd_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq, Hkv,
+                                                     D, dtc, stream)),
+            ("attn_bwd_main", L.attn_bwd_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
+                                                p(self.dk), p(self.dv), p(self.ws), nws, B, T, Hq, Hkv, D,
+                                                scale, dtc, stream)),
+            ("attn_bwd_dq_finalize", L.attn_bwd_dq_finalize, (p(self.ws), nws, p(self.dq), B, T, Hq, Hkv, D,
+                                                              scale, dtc, stream)),
+            ("rope_inv_dq", L.rope_apply, (p(self.dq), p(self.dq_raw), B, T, Hq, D, dtc, base, 0, 1, stream)),
+            ("rope_inv_dk", L.rope_apply, (p(self.dk), p(self.dk_raw), B, T, Hkv, D, dtc, base, 0, 1, stream)),
+        ]
+
+    def run(self):
+        for name, fn, args in self.calls:
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError("%s returned status %d" % (name, st))
+
+    def run_with_events(self, torch, events):
+        for (name, fn, args), (e0, e1) in zip(self.calls, events):
+            e0.record()
+            st = fn(*args)
+            e1.record()
+            if st != 0:
+                raise RuntimeError("%s returned status %d" % (name, st))
+
+
+def algorithmic(w) -> dict:
+    """Per-launch algorithmic FLOPs / bytes of each kernel of the step."""
+    es = 4 if w.dtype == "f32" else 2
+    qb = w.B * w.T * w.Hq * w.D * es
+    kb = w.B * w.T * w.Hkv * w.D * es
+    lse = w.B * w.Hq * w.T * 4
+    return {
+        "rope_q": {"bytes": 2 * qb}, "rope_k": {"bytes": 2 * kb},
+        "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
+        "attn_bwd_pre": {"bytes": 2 * qb + lse + w.B * w.T * w.Hq * w.D * 4},
+        "attn_bwd_main": {"flops": w.flops_bwd(), "bytes": 2 * qb + 2 * kb + 2 * lse + 2 * kb
+                          + w.B * w.T * w.Hq * w.D * 4},
+        "attn_bwd_dq_finalize": {"bytes": w.B * w.T * w.Hq * w.D * 4 + qb},
+        "rope_inv_dq": {"bytes": 2 * qb}, "rope_inv_dk": {"bytes": 2 * kb},
+    }
+
+
+def time_workload(name, steps, warmup, torch, ea, W):
+    w = W.WORKLOADS[name]
+    log("[bench] workload %s: generating inputs" % name)
+    inp = W.make_inputs(w)
+    step = Step(w, inp, torch, ea)
+    log("[bench] %s: %d warmup steps" % (name, warmup))
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    log("[bench] %s: timing %d steps" % (name, steps))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step.run()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+    # Per-kernel durations: the same steps again with HIP events around every launch, on the
+    # stream the kernels are launched on (the current stream).
+    log("[bench] %s: per-kernel events over %d steps" % (name, steps))
+    per = {n: [] for n, _, _ in step.calls}
+    for _ in range(steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in step.calls]
+        step.run_with_events(torch, ev)
+        torch.cuda.synchronize()
+        for (n, _, _), (a, b) in zip(step.calls, ev):
+            per[n].append(a.elapsed_time(b))
+    kern_us = {n: 1000.0 * statistics.mean(v) for n, v in per.items()}
+    return w, step, ms, wall, kern_us
+
+
+def roofline_for(w, kern_us, name):
+    alg = algorithmic(w)[name]
+    dur_s = kern_us[name] * 1e-6
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+        ent = tc.get("kernels", {}).get(name)
+        if (ent and ent.get("workload") == w.name and name in KERNEL_SOURCES
+                and ent.get("source_sha") == sources_sha(KERNEL_SOURCES[name])):
+            traffic = ent.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        traffic = None
+    if "flops" in alg:
+        achieved = alg["flops"] / dur_s / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": alg["flops"], "algorithmic_bytes_per_launch": alg["bytes"],
+                "avg_launch_us": round(kern_us[name], 2)}
+    achieved = alg["bytes"] / dur_s / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg["bytes"], "avg_launch_us": round(kern_us[name], 2)}
+
+
+def cpu_baseline(w, W):
+    """The oracle (plain float64 C++, OpenMP) on the host cores: one whole step of the same
+    workload (RoPE on Q and K, forward, analytic backward, inverse RoPE on dQ and dK)."""
+    from oracle import oracle
+    inp = W.make_inputs(w)
+    import numpy as np
+    arrs = {k: np.ascontiguousarray(v.to(dtype=__import__("torch").float64).numpy())
+            for k, v in inp.items() if k != "peaky"}
+    times = []
+    budget = 30.0
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        qr = oracle.rope(arrs["q_raw"], w.base)
+        kr = oracle.rope(arrs["k_raw"], w.base)
+        oracle.attn_fwd(qr, kr, arrs["v"])
+        dq, dk, _ = oracle.attn_bwd(qr, kr, arrs["v"], arrs["dout"])
+        oracle.rope(dq, w.base, inverse=True)
+        oracle.rope(dk, w.base, inverse=True)
+        times.append(time.perf_counter() - t0)
+        spent = time.perf_counter() - t_all
+        if len(times) >= 3 or spent + times[-1] > budget or spent > 10.0:
+            break
+    t = statistics.median(times)
+    return {"value": round(w.flops_total() / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole step of workload %s (RoPE q/k, fwd, analytic bwd, inverse RoPE), float64, "
+                      "median of %d run(s), %.2f s each" % (w.name, len(times), t),
+            "seconds_per_step": round(t, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="blog_t1024")
+    ap.add_argument("--extra", default="long_t8192",
+                    help="comma-separated extra workloads timed the same way (reported under 'extra')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import causal_gqa_attention_fwd_amd as ea
+    from causal_gqa_attention_fwd_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    ea.lib()  # fail loudly when the HIP library is missing
+
+    w, step, ms, wall, kern_us = time_workload(args.workload, args.steps, args.warmup, torch, ea, W)
+    tflops = w.flops_total() / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    dominant = max(kern_us, key=kern_us.get)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": dict(w.describe(), causal=True,
+                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_main,attn_bwd_dq_finalize,"
+                            "rope_inv_dq,rope_inv_dk"),
+        "frac_of_peak": round(tflops / peak, 4),
+        "flops_per_step": w.flops_total(),
+        "flops_convention": "exact causal: 14*D*B*Hq*T(T+1)/2",
+        "host_wall_s": round(wall, 4),
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "roofline": roofline_for(w, kern_us, dominant),
+        "roofline_attn_fwd": roofline_for(w, kern_us, "attn_fwd"),
+    }
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
+        steps = max(5, args.steps // 5)
+        we, _, mse, _, ke = time_workload(name, steps, max(2, args.warmup // 5), torch, ea, W)
+        tf = we.flops_total() / (mse * 1e-3) / 1e12
+        extra[name] = {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(mse, 4),
+                       "frac_of_peak": round(tf / PEAK_TFLOPS[we.dtype], 4), "steps": steps,
+                       "kernel_us": {k: round(v, 2) for k, v in ke.items()}}
+    out["extra"] = extra
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) on host cores")
+        out["cpu_baseline"] = cpu_baseline(w, W)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,230 @@
+"""causal_gqa_attention_fwd_amd -- Python binding of libeuler_attn (gfx950 / MI355X).
+
+Causal grouped-query attention with rotary embeddings, forward and backward, as
+hand-written HIP kernels behind a C ABI (``include/euler_attn.h``).  This module only
+marshals arguments: torch supplies device memory and the current stream, every step of the
+computation runs in the library's kernels.  There is no fallback: if the library is not
+built, or the tensors are not on a ROCm device, the calls raise.
+
+    rope_apply(x, base=1e4, pos0=0, inverse=False, out=None) -> y
+    attn_fwd(q, k, v, scale=None, out=None, lse=None)        -> (o, lse)
+    attn_bwd(q, k, v, o, lse, dout, scale=None, ...)         -> (dq, dk, dv)
+
+Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
+dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
+           "attn_bwd_main", "attn_bwd_dq_finalize", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
+EA_F32, EA_BF16 = 0, 1
+STATUS = {0: "EA_OK", 1: "EA_ERR_NULL", 2: "EA_ERR_INVALID_ARG", 3: "EA_ERR_UNSUPPORTED",
+          4: "EA_ERR_ALIGN", 5: "EA_ERR_ALIAS", 6: "EA_ERR_WORKSPACE", 7: "EA_ERR_HIP"}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libeuler_attn.so (built in-tree by ``python -m causal_gqa_attention_fwd_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libeuler_attn.so is not built (%s); run "
+                           "`python -m causal_gqa_attention_fwd_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, cd, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
+    L.rope_apply.argtypes = [vp, vp, ci, ci, ci, ci, ci, cd, ci, ci, vp]
+    L.rope_apply.restype = ci
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_fwd.restype = ci
+    L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_bwd_workspace_size.restype = sz
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd.restype = ci
+    L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, vp]
+    L.attn_bwd_preprocess.restype = ci
+    L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_main.restype = ci
+    L.attn_bwd_dq_finalize.argtypes = [vp, sz, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_dq_finalize.restype = ci
+    L.euler_attn_status_string.argtypes = [ci]
+    L.euler_attn_status_string.restype = ctypes.c_char_p
+    L.euler_attn_version.argtypes = []
+    L.euler_attn_version.restype = ci
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return EA_F32
+    if t.dtype == torch.bfloat16:
+        return EA_BF16
+    raise TypeError("euler_attn supports float32 and bfloat16 tensors, got %s" % t.dtype)
+
+
+def _check(name: str, t: torch.Tensor, ndim: int, device=None, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise RuntimeError("%s must be on a ROCm GPU device (got %s); there is no CPU path"
+                           % (name, t.device))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _raise(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().euler_attn_status_string(status).decode()
+        raise RuntimeError("%s failed: %s" % (what, msg))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def rope_apply(x: torch.Tensor, base: float = 10000.0, pos0: int = 0, inverse: bool = False,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rotary embedding of x [B, T, H, D] (adjacent pairs, angle (pos0+t)*base^(-2i/D))."""
+    _check("x", x, 4)
+    y = torch.empty_like(x) if out is None else out
+    _check("out", y, 4, x.device, x.dtype)
+    if y.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    B, T, H, D = x.shape
+    with torch.cuda.device(x.device):
+        st = lib().rope_apply(x.data_ptr(), y.data_ptr(), B, T, H, D, _dtype_code(x), float(base),
+                              int(pos0), int(bool(inverse)), _stream(x.device))
+    _raise(st, "rope_apply")
+    return y
+
+
+def _shapes(q, k, v):
+    _check("q", q, 4)
+    _check("k", k, 4, q.device, q.dtype)
+    _check("v", v, 4, q.device, q.dtype)
+    B, T, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError("k and v must be [B, T, Hkv, D] matching q [B, T, Hq, D]")
+    return B, T, Hq, k.shape[2], D
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Causal GQA attention forward; returns (o [B,T,Hq,D], lse [B,Hq,T] float32)."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    _check("out", o, 4, q.device, q.dtype)
+    if o.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    l = torch.empty((B, Hq, T), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check("lse", l, 3, q.device, torch.float32)
+    if tuple(l.shape) != (B, Hq, T):
+        raise ValueError("lse must be [B, Hq, T]")
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                            B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_fwd")
+    return o, l
+
+
+def attn_bwd_workspace_size(B: int, T: int, Hq: int, Hkv: int, D: int, dtype=torch.bfloat16) -> int:
+    code = EA_F32 if dtype == torch.float32 else EA_BF16
+    return int(lib().attn_bwd_workspace_size(B, T, Hq, Hkv, D, code))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
+             workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
+             dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Causal GQA attention backward; returns (dq, dk, dv), dk/dv summed over each group."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    _check("o", o, 4, q.device, q.dtype)
+    _check("dout", dout, 4, q.device, q.dtype)
+    _check("lse", lse, 3, q.device, torch.float32)
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("o/dout must match q and lse must be [B, Hq, T]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check(name, t, 4, q.device, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError("%s has the wrong shape" % name)
+    need = int(lib().attn_bwd_workspace_size(B, T, Hq, Hkv, D, _dtype_code(q)))
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            workspace.data_ptr(), nbytes, B, T, Hq, Hkv, D, float(scale),
+                            _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def _ws_args(workspace: torch.Tensor, device) -> tuple:
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of the inputs")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, workspace: torch.Tensor, Hkv: int) -> None:
+    """Backward stage 1: D_t = sum_d dout * o into the workspace; zero the dQ accumulator."""
+    _check("o", o, 4)
+    _check("dout", dout, 4, o.device, o.dtype)
+    B, T, Hq, D = o.shape
+    wp, wb = _ws_args(workspace, o.device)
+    with torch.cuda.device(o.device):
+        st = lib().attn_bwd_preprocess(o.data_ptr(), dout.data_ptr(), wp, wb, B, T, Hq, Hkv, D,
+                                       _dtype_code(o), _stream(o.device))
+    _raise(st, "attn_bwd_preprocess")
+
+
+def attn_bwd_main(q, k, v, lse, dout, workspace, dk, dv, scale: float | None = None) -> None:
+    """Backward stage 2: dk, dv (group-summed, overwritten) and the dQ accumulator."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    wp, wb = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                 dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb, B, T, Hq,
+                                 Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd_main")
+
+
+def attn_bwd_dq_finalize(workspace: torch.Tensor, dq: torch.Tensor, Hkv: int,
+                         scale: float | None = None) -> None:
+    """Backward stage 3: dq = scale * accumulator, in dq's dtype."""
+    _check("dq", dq, 4)
+    B, T, Hq, D = dq.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    wp, wb = _ws_args(workspace, dq.device)
+    with torch.cuda.device(dq.device):
+        st = lib().attn_bwd_dq_finalize(wp, wb, dq.data_ptr(), B, T, Hq, Hkv, D, float(scale),
+                                        _dtype_code(dq), _stream(dq.device))
+    _raise(st, "attn_bwd_dq_finalize")

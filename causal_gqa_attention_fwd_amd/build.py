@@ -1,0 +1,72 @@
+"""Build libeuler_attn.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+Usage: python -m causal_gqa_attention_fwd_amd.build      (or build() from Python)
+
+Every HIP source is compiled with hipcc for gfx950 only, with packed-fp32 VALU
+instructions disabled, into causal_gqa_attention_fwd_amd/_build/, and linked into
+causal_gqa_attention_fwd_amd/libeuler_attn.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libeuler_attn.so")
+SOURCES = ["api.hip", "rope.hip", "attn_fwd.hip", "attn_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"),
+                 shutil.which("hipcc") or ""):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+COMMON_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
+    # Packed fp32 VALU ops are kept out of every kernel.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE, "-I" + CSRC,
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, res.stdout))
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all HIP sources and link libeuler_attn.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % res.stdout)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

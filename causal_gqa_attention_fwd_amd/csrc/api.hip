@@ -1,0 +1,215 @@
+// api.hip -- the C ABI of libeuler_attn: argument validation and dispatch.
+//
+// Every entry point validates all of its arguments before anything is enqueued (no HIP
+// call happens on an invalid call), then hands off to the internal launchers.  Nothing is
+// allocated, freed or synchronised here.  Declarations and the contract: euler_attn.h.
+#include <cmath>
+#include <cstdint>
+
+#include "ea_kernels.h"
+#include "euler_attn.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+size_t elem_size(ea_dtype dt) { return dt == EA_F32 ? 4 : 2; }
+
+bool dtype_ok(int dt) { return dt == EA_F32 || dt == EA_BF16; }
+
+bool attn_dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
+
+ea_status from_hip(hipError_t e) { return e == hipSuccess ? EA_OK : EA_ERR_HIP; }
+
+// Shared checks of attn_fwd / attn_bwd sizes.
+ea_status check_attn_sizes(int B, int T, int Hq, int Hkv, int D, float scale, int dt) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return EA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return EA_ERR_INVALID_ARG;
+    if (!dtype_ok(dt) || !attn_dim_ok(D)) return EA_ERR_UNSUPPORTED;
+    // The kernels index with 64-bit arithmetic but launch 1-D grids of 32-bit size.
+    if ((long long)B * Hq > (1LL << 24) || T > (1 << 28)) return EA_ERR_UNSUPPORTED;
+    return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* euler_attn_status_string(ea_status s) {
+    switch (s) {
+        case EA_OK: return "EA_OK: success";
+        case EA_ERR_NULL: return "EA_ERR_NULL: a required pointer is NULL";
+        case EA_ERR_INVALID_ARG: return "EA_ERR_INVALID_ARG: a size, count, scale, base or flag is out of range";
+        case EA_ERR_UNSUPPORTED: return "EA_ERR_UNSUPPORTED: head_dim or dtype not supported";
+        case EA_ERR_ALIGN: return "EA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        case EA_ERR_ALIAS: return "EA_ERR_ALIAS: an output overlaps an input or another output";
+        case EA_ERR_WORKSPACE: return "EA_ERR_WORKSPACE: workspace smaller than attn_bwd_workspace_size()";
+        case EA_ERR_HIP: return "EA_ERR_HIP: the HIP runtime reported an error at launch";
+    }
+    return "unknown euler_attn status";
+}
+
+int euler_attn_version(void) { return kVersion; }
+
+ea_status rope_apply(const void* x, void* y, int B, int T, int H, int D, ea_dtype dt,
+                     double base, int pos0, int inverse, hipStream_t stream) {
+    if (x == nullptr || y == nullptr) return EA_ERR_NULL;
+    if (B < 1 || T < 1 || H < 1 || D < 2 || (D % 2) != 0 || pos0 < 0) return EA_ERR_INVALID_ARG;
+    if (!std::isfinite(base) || !(base > 1.0) || (inverse != 0 && inverse != 1)) return EA_ERR_INVALID_ARG;
+    if (!dtype_ok(dt) || D > 256 || (D % 8) != 0) return EA_ERR_UNSUPPORTED;
+    if ((long long)pos0 + T > (1LL << 31)) return EA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y)) return EA_ERR_ALIGN;
+    const size_t bytes = (size_t)B * T * H * D * elem_size(dt);
+    if (x != y && overlap(range(x, bytes), range(y, bytes))) return EA_ERR_ALIAS;
+    return from_hip(ea::launch_rope(x, y, B, T, H, D, static_cast<ea::IoType>(dt), base, pos0,
+                                    inverse, stream));
+}
+
+ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const Range rq = range(q, (size_t)B * T * Hq * D * es);
+    const Range rk = range(k, (size_t)B * T * Hkv * D * es);
+    const Range rv = range(v, (size_t)B * T * Hkv * D * es);
+    const Range ro = range(o, (size_t)B * T * Hq * D * es);
+    const Range rl = range(lse, (size_t)B * Hq * T * sizeof(float));
+    for (Range out : {ro, rl})
+        for (Range in : {rq, rk, rv})
+            if (overlap(out, in)) return EA_ERR_ALIAS;
+    if (overlap(ro, rl)) return EA_ERR_ALIAS;
+    return from_hip(ea::launch_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale,
+                                        static_cast<ea::IoType>(dt), stream));
+}
+
+size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1 || !dtype_ok(dt)) return 0;
+    return ea::bwd_workspace_bytes(B, T, Hq, D);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct BwdSizes {
+    size_t qb, kb, lseb, ws;
+};
+
+BwdSizes bwd_sizes(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
+    const size_t es = elem_size(dt);
+    return BwdSizes{(size_t)B * T * Hq * D * es, (size_t)B * T * Hkv * D * es,
+                    (size_t)B * Hq * T * sizeof(float), ea::bwd_workspace_bytes(B, T, Hq, D)};
+}
+
+ea_status check_workspace(const void* ws, size_t bytes, size_t need) {
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EA_ERR_ALIGN;
+    if (bytes < need) return EA_ERR_WORKSPACE;
+    return EA_OK;
+}
+
+template <size_t NI, size_t NO>
+ea_status check_alias(const Range (&ins)[NI], const Range (&outs)[NO]) {
+    for (const Range& out : outs)
+        for (const Range& in : ins)
+            if (overlap(out, in)) return EA_ERR_ALIAS;
+    for (size_t a = 0; a < NO; ++a)
+        for (size_t c = a + 1; c < NO; ++c)
+            if (overlap(outs[a], outs[c])) return EA_ERR_ALIAS;
+    return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
+                   ea_dtype dt, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {q, k, v, o, static_cast<const void*>(lse), dout,
+                          static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(o, z.qb),
+                         range(lse, z.lseb), range(dout, z.qb)};
+    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb), range(workspace, z.ws)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, T, Hq,
+                                        Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
+}
+
+ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                              ea_dtype dt, hipStream_t stream) {
+    if (!o || !dout || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, 1.0f, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(o) || !aligned16(dout)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(o, z.qb), range(dout, z.qb)};
+    const Range outs[] = {range(workspace, z.ws)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_pre(o, dout, workspace, B, T, Hq, D,
+                                       static_cast<ea::IoType>(dt), stream));
+}
+
+ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                        float scale, ea_dtype dt, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dout || !dk || !dv || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {q, k, v, static_cast<const void*>(lse), dout,
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(lse, z.lseb),
+                         range(dout, z.qb)};
+    const Range outs[] = {range(dk, z.kb), range(dv, z.kb), range(workspace, z.ws)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_main(q, k, v, lse, dout, dk, dv, workspace, B, T, Hq, Hkv, D,
+                                        scale, static_cast<ea::IoType>(dt), stream));
+}
+
+ea_status attn_bwd_dq_finalize(const void* workspace, size_t workspace_bytes, void* dq, int B,
+                               int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                               hipStream_t stream) {
+    if (!workspace || !dq) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(dq)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(workspace, z.ws)};
+    const Range outs[] = {range(dq, z.qb)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_dq_finalize(workspace, dq, B, T, Hq, D, scale,
+                                               static_cast<ea::IoType>(dt), stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// ea_common.h -- device-side building blocks shared by the libeuler_attn kernels (gfx950).
+//
+// MFMA operand layouts used throughout (64-lane wavefront, lane l, half h = l >> 5):
+//  * v_mfma_f32_32x32x16_bf16 (bf16) and v_mfma_f32_32x32x2_f32 (fp32) both compute a
+//    32 x 32 fp32 tile C += A * B.  A lane supplies row (l & 31) of A and column (l & 31)
+//    of B, KPL contraction elements each (8 for bf16, 1 for fp32).  Which contraction
+//    index a (half, element) slot carries is our choice, as long as A and B agree.
+//  * C: lane l holds column (l & 31); its register r (0..15) holds row
+//    acc_row(r, h) = 8 * (r / 4) + 4 * h + (r % 4).
+//
+// Two contraction mappings are used:
+//  * "split" (over a contiguous dimension of length L, e.g. head_dim): instruction s, half
+//    h, element e  <->  index h * L/2 + s * KPL + e.  A lane's elements are one contiguous
+//    run of L/2, so its operand is read with wide loads.
+//  * "accumulator" (over the 32 rows of a C tile reused as an operand): instruction s,
+//    half h, element e  <->  register r = s * KPL + e  <->  row acc_row(r, h).  The partner
+//    operand is stored in LDS in "slot" order slot = 16 * h + r, so a lane again reads one
+//    contiguous run of 16 elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ea {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<float> {
+    typedef float frag;
+    static constexpr int KPL = 1;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<bf16> {
+    typedef bf16x8 frag;
+    static constexpr int KPL = 8;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Row of a 32x32 accumulator held by register r of a lane in half h.
+__device__ __host__ constexpr inline int acc_row(int r, int h) {
+    return 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+// LDS slot of row k (0..31) of an accumulator-ordered operand: 16 * half + register.
+__device__ __host__ constexpr inline int acc_slot(int k) {
+    return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
+}
+
+// Fragment load of KPL contiguous elements from LDS or global memory.
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_frag(const T* p);
+
+template <>
+__device__ inline float load_frag<float>(const float* p) {
+    return *p;
+}
+
+template <>
+__device__ inline bf16x8 load_frag<bf16>(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Convert fp32 values (registers r0 .. r0+KPL-1 of an accumulator) into an operand fragment.
+template <typename T>
+__device__ inline typename Mfma<T>::frag acc_to_frag(const f32x16& c, int r0);
+
+template <>
+__device__ inline float acc_to_frag<float>(const f32x16& c, int r0) {
+    return c[r0];
+}
+
+template <>
+__device__ inline bf16x8 acc_to_frag<bf16>(const f32x16& c, int r0) {
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)c[r0 + e];  // round to nearest even
+    return f;
+}
+
+template <typename T>
+__device__ inline float to_f32(T x) {
+    return (float)x;
+}
+
+template <typename T>
+__device__ inline T from_f32(float x) {
+    return (T)x;
+}
+
+// 16-byte vector of I/O elements.
+template <typename T>
+struct Vec16 {
+    static constexpr int N = 16 / sizeof(T);
+    u32x4 raw;
+    __device__ inline T get(int i) const {
+        return reinterpret_cast<const T*>(&raw)[i];
+    }
+    __device__ inline void set(int i, T v) {
+        reinterpret_cast<T*>(&raw)[i] = v;
+    }
+};
+
+template <typename T>
+__device__ inline Vec16<T> ld16(const T* p) {
+    Vec16<T> v;
+    v.raw = *reinterpret_cast<const u32x4*>(p);
+    return v;
+}
+
+template <typename T>
+__device__ inline void st16(T* p, const Vec16<T>& v) {
+    *reinterpret_cast<u32x4*>(p) = v.raw;
+}
+
+template <typename T>
+__device__ inline Vec16<T> zero16() {
+    Vec16<T> v;
+    v.raw = u32x4{0u, 0u, 0u, 0u};
+    return v;
+}
+
+__device__ inline f32x16 zero_acc() {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+    return z;
+}
+
+__device__ inline float xor_shfl32(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+}  // namespace ea

@@ -1,0 +1,41 @@
+// ea_kernels.h -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ea {
+
+enum IoType { kF32 = 0, kBF16 = 1 };
+
+// RoPE of x [B, T, H, D] into y; see rope_apply in euler_attn.h.
+hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoType dt,
+                       double base, int pos0, int inverse, hipStream_t stream);
+
+// Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log).
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
+                           hipStream_t stream);
+
+// Workspace layout of the backward: [dq accumulator fp32 | D_t fp32], 256-byte aligned parts.
+size_t bwd_workspace_bytes(int B, int T, int Hq, int D);
+
+// Backward stages (their composition is launch_attn_bwd):
+//   pre:      D_t = sum_d dout * o into the workspace, dq accumulator zeroed;
+//   main:     dk, dv written, dq accumulator filled;
+//   finalize: dq = scale * accumulator in the I/O dtype.
+hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
+                          int D, IoType dt, hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, void* dk, void* dv, void* workspace, int B, int T,
+                           int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream);
+hipError_t launch_bwd_dq_finalize(const void* workspace, void* dq, int B, int T, int Hq, int D,
+                                  float scale, IoType dt, hipStream_t stream);
+
+// Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above.
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
+                           IoType dt, hipStream_t stream);
+
+}  // namespace ea

@@ -1,0 +1,141 @@
+/*
+ * euler_attn.h -- C ABI of libeuler_attn: causal grouped-query attention with rotary
+ * position embeddings, forward and backward, as hand-written HIP kernels for gfx950.
+ *
+ * What is computed (sources: the web pages describing NanoEuler's training engine):
+ *  - Rotary embeddings on queries and keys ("Show HN: NanoEuler", section 2 "模型组件";
+ *    "Tiny Hackable CUDA Language Model Implementation", section 1 "架构设计").
+ *  - Causal scaled dot-product attention: query t sees keys s <= t ("Tiny Hackable ...",
+ *    section 1), with several query heads sharing one key/value head (GQA, "Show HN:
+ *    NanoEuler", section 2).
+ *  - Computed tile by tile with an online softmax so that the T x T score matrix is never
+ *    stored ("Show HN: NanoEuler", section 4 "硬件与性能"; the blog's "Tiled
+ *    FlashAttention" section), in forward and in backward (both hand-written and
+ *    gradient-checked, "Show HN: NanoEuler", section 3).
+ *
+ * Conventions shared by every call:
+ *  - Q, O, dO, dQ are [B, T, Hq, D]; K, V, dK, dV are [B, T, Hkv, D]; all contiguous,
+ *    row-major, D fastest, element type `dt`.  LSE is [B, Hq, T] float32 (natural log).
+ *  - Query head h uses key/value head floor(h / g), g = Hq / Hkv.
+ *  - The causal mask keeps key s for query t iff s <= t (diagonal included).
+ *  - All pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *    frees or synchronises; work is enqueued on `stream` (NULL = the null stream) and the
+ *    call returns after the enqueue.  Asynchronous device faults surface at the caller's
+ *    next synchronisation.
+ *  - Argument validation happens before anything is enqueued: on any error the call
+ *    returns the status below and writes nothing.
+ *  - Every tensor pointer must be 16-byte aligned.  All index arithmetic is 64-bit.
+ */
+#ifndef EULER_ATTN_H
+#define EULER_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EA_OK = 0,
+    EA_ERR_NULL = 1,          /* a required pointer is NULL                               */
+    EA_ERR_INVALID_ARG = 2,   /* a size, count, scale, base or flag is out of range       */
+    EA_ERR_UNSUPPORTED = 3,   /* valid but not built: head_dim or dtype                   */
+    EA_ERR_ALIGN = 4,         /* a tensor pointer is not 16-byte aligned                  */
+    EA_ERR_ALIAS = 5,         /* an output overlaps an input or another output            */
+    EA_ERR_WORKSPACE = 6,     /* workspace smaller than attn_bwd_workspace_size()         */
+    EA_ERR_HIP = 7            /* the HIP runtime reported an error at launch              */
+} ea_status;
+
+typedef enum {
+    EA_F32 = 0,   /* float32 I/O; contractions on fp32 MFMA, fp32 softmax               */
+    EA_BF16 = 1   /* bfloat16 I/O; contractions on bf16 MFMA with fp32 accumulation,    */
+                  /* every fp32 -> bf16 conversion rounds to nearest even                */
+} ea_dtype;
+
+/*
+ * rope_apply -- rotary position embedding of x [B, T, H, D] into y (same shape and dtype).
+ * For each row (b, t, h) and each adjacent pair (x[2i], x[2i+1]), i in [0, D/2), rotate by
+ * phi = (pos0 + t) * base^(-2i/D):  y[2i] = x[2i] cos phi - x[2i+1] sin phi,
+ * y[2i+1] = x[2i] sin phi + x[2i+1] cos phi.  inverse = 1 rotates by -phi, which is the
+ * backward of the forward rotation (the rotation is orthogonal): apply it to dQ and dK to
+ * obtain gradients with respect to the pre-RoPE tensors.  The angle is formed and reduced
+ * modulo 2*pi in float64; sin/cos of the reduced angle and the rotation are float32.
+ * y == x (exactly) is allowed (in place); any other overlap is EA_ERR_ALIAS.
+ * Errors: NULL x or y; B, T, H < 1, D odd or < 2, pos0 < 0, base <= 1 or not finite,
+ * inverse not 0/1 (EA_ERR_INVALID_ARG); D > 256 or unknown dt (EA_ERR_UNSUPPORTED).
+ */
+ea_status rope_apply(const void* x, void* y, int B, int T, int H, int D, ea_dtype dt,
+                     double base, int pos0, int inverse, hipStream_t stream);
+
+/*
+ * attn_fwd -- causal GQA attention forward.  For every batch b, query head h and query
+ * position t:  S_ts = scale * <q_t, k_s> for s <= t;  O_t = sum_s softmax_s(S_t.) v_s;
+ * LSE_t = log sum_{s<=t} exp(S_ts).  q and k are expected to carry RoPE already.
+ * Outputs: o [B, T, Hq, D] in dt; lse [B, Hq, T] float32 (needed by attn_bwd).
+ * Errors: NULL pointer; B, T, Hq, Hkv < 1, Hq % Hkv != 0, scale not finite or <= 0
+ * (EA_ERR_INVALID_ARG); D not in {32, 64, 128} or unknown dt (EA_ERR_UNSUPPORTED);
+ * misalignment (EA_ERR_ALIGN); o or lse overlapping q, k, v or each other (EA_ERR_ALIAS).
+ */
+ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                   hipStream_t stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device scratch attn_bwd needs: a float32 dQ
+ * accumulator [B, T, Hq, D] and the per-row D_t = sum_d dO * O [B, Hq, T] float32, each
+ * rounded up to 256 bytes.  Linear in T (never T^2).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt);
+
+/*
+ * attn_bwd -- causal GQA attention backward (gradients of sum(dout * O)).  Inputs are the
+ * forward's q, k, v, o, lse and the upstream gradient dout [B, T, Hq, D].  Outputs, all
+ * overwritten (not accumulated):  dq [B, T, Hq, D];  dk, dv [B, T, Hkv, D], each summed
+ * over the g query heads that share the K/V head.  The softmax is recomputed tile by tile
+ * from lse; D_t = sum_d dout * o.  dq is accumulated in float32 with atomics across key
+ * tiles, so its last bits may differ from run to run; o, lse, dk and dv are deterministic.
+ * workspace: device memory of at least attn_bwd_workspace_size(...) bytes, 256-byte
+ * aligned, contents on entry ignored, clobbered on return.
+ * Errors: as attn_fwd; dq/dk/dv/workspace overlapping any input or each other
+ * (EA_ERR_ALIAS); workspace NULL or too small (EA_ERR_NULL / EA_ERR_WORKSPACE).
+ */
+ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv,
+                   int D, float scale, ea_dtype dt, hipStream_t stream);
+
+/*
+ * The three stages of attn_bwd, for callers that schedule them separately (attn_bwd is
+ * exactly attn_bwd_preprocess, attn_bwd_main, attn_bwd_dq_finalize on one stream).  They
+ * share attn_bwd's workspace, which carries the state from one stage to the next, and take
+ * the same sizes; each validates its own pointers and sizes like attn_bwd.
+ *  - attn_bwd_preprocess: D_t = sum_d dout * o for every (b, h, t), and the float32 dQ
+ *    accumulator set to zero.  Reads o, dout; writes only the workspace.
+ *  - attn_bwd_main: the recomputed softmax, dP, dS; writes dk and dv (overwritten,
+ *    group-summed) and adds every dQ contribution into the accumulator.  Needs the
+ *    preprocess stage's workspace contents.
+ *  - attn_bwd_dq_finalize: dq = scale * accumulator, rounded to dt.
+ */
+ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                              ea_dtype dt, hipStream_t stream);
+ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                        float scale, ea_dtype dt, hipStream_t stream);
+ea_status attn_bwd_dq_finalize(const void* workspace, size_t workspace_bytes, void* dq, int B,
+                               int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                               hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* euler_attn_status_string(ea_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int euler_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EULER_ATTN_H */

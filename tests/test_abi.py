@@ -1,0 +1,162 @@
+"""The C ABI of libeuler_attn, on the CPU: the library loads, exports every symbol the
+header declares, and rejects invalid calls with the documented status before touching the
+device (validation never dereferences a pointer, so fake addresses are used here).
+No call in this file reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_gqa_attention_fwd_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "euler_attn.h")
+
+OK, NULL, INVALID, UNSUP, ALIGN, ALIAS, WS, HIP = range(8)
+F32, BF16 = 0, 1
+A = 1 << 32  # fake, 256-byte aligned "device" addresses, far apart
+
+
+def fake(n):
+    return A * (n + 1)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ea.LIB_PATH):
+        pytest.skip("libeuler_attn.so not built")
+    return ea.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
+              "euler_attn_status_string", "euler_attn_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for code in range(8):
+        s = L.euler_attn_status_string(code).decode()
+        assert s.startswith(ea.STATUS[code])
+    assert L.euler_attn_version() >= 100
+
+
+def rope(L, x=fake(0), y=fake(1), B=1, T=4, H=2, D=64, dt=BF16, base=1e4, pos0=0, inv=0):
+    return L.rope_apply(x, y, B, T, H, D, dt, base, pos0, inv, None)
+
+
+def test_rope_validation(L):
+    assert rope(L, x=None) == NULL
+    assert rope(L, y=None) == NULL
+    for kw in (dict(B=0), dict(T=0), dict(H=0), dict(D=7), dict(D=0), dict(pos0=-1),
+               dict(base=1.0), dict(base=float("nan")), dict(base=float("inf")), dict(inv=2)):
+        assert rope(L, **kw) == INVALID, kw
+    assert rope(L, D=258) == UNSUP
+    assert rope(L, D=6) == UNSUP          # not a multiple of 8
+    assert rope(L, dt=5) == UNSUP
+    assert rope(L, x=fake(0) + 4) == ALIGN
+    assert rope(L, y=fake(0) + 16) == ALIAS  # partial overlap
+    # y == x is allowed: it passes validation (and would launch), so not called here.
+
+
+def fwd(L, q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), B=2, T=16, Hq=4, Hkv=2,
+        D=64, scale=0.125, dt=BF16):
+    return L.attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, None)
+
+
+def test_fwd_validation(L):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(L, **{name: None}) == NULL, name
+    for kw in (dict(B=0), dict(T=0), dict(Hq=0), dict(Hkv=0), dict(Hq=3, Hkv=2),
+               dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf"))):
+        assert fwd(L, **kw) == INVALID, kw
+    for D in (16, 48, 96, 256):
+        assert fwd(L, D=D) == UNSUP
+    assert fwd(L, dt=3) == UNSUP
+    assert fwd(L, v=fake(2) + 8) == ALIGN
+    assert fwd(L, lse=fake(4) + 4) == ALIGN
+    assert fwd(L, o=fake(0)) == ALIAS
+    assert fwd(L, lse=fake(1) + 256) == ALIAS
+    assert fwd(L, lse=fake(3) + 1024) == ALIAS   # lse inside o
+
+
+def test_workspace_size(L):
+    # fp32 dq accumulator + fp32 D_t, each rounded to 256 bytes; linear in T.
+    def ws(B, T, Hq, Hkv, D, dt=BF16):
+        return L.attn_bwd_workspace_size(B, T, Hq, Hkv, D, dt)
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    assert ws(4, 1024, 12, 4, 64) == up(4 * 1024 * 12 * 64 * 4) + up(4 * 12 * 1024 * 4)
+    assert ws(1, 3, 1, 1, 32) == up(3 * 32 * 4) + up(3 * 4)
+    assert ws(8, 4096, 32, 8, 128) == 2 * ws(8, 2048, 32, 8, 128)
+    assert ws(0, 4, 1, 1, 32) == 0
+    assert ws(1, 4, 3, 2, 32) == 0
+
+
+def bwd(L, q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), do=fake(5), dq=fake(6),
+        dk=fake(7), dv=fake(8), ws=fake(9), wsb=None, B=2, T=16, Hq=4, Hkv=2, D=64, scale=0.125,
+        dt=BF16):
+    if wsb is None:
+        wsb = L.attn_bwd_workspace_size(B, T, Hq, Hkv, D, dt)
+    return L.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, wsb, B, T, Hq, Hkv, D, scale, dt, None)
+
+
+def test_bwd_validation(L):
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert bwd(L, **{name: None}) == NULL, name
+    for kw in (dict(B=0), dict(T=0), dict(Hq=6, Hkv=4), dict(scale=0.0)):
+        assert bwd(L, **kw) == INVALID, kw
+    assert bwd(L, D=80) == UNSUP
+    assert bwd(L, dk=fake(7) + 2) == ALIGN
+    assert bwd(L, ws=fake(9) + 16) == ALIGN          # workspace needs 256-byte alignment
+    assert bwd(L, wsb=1024) == WS
+    assert bwd(L, dq=fake(0)) == ALIAS                # output over an input
+    assert bwd(L, dv=fake(7)) == ALIAS                # two outputs
+    assert bwd(L, ws=fake(6)) == ALIAS                # workspace over an output
+
+
+def test_bwd_stage_validation(L):
+    ws = L.attn_bwd_workspace_size(2, 16, 4, 2, 64, BF16)
+    pre = lambda o=fake(0), do=fake(1), w=fake(2), wb=ws, D=64, Hq=4: L.attn_bwd_preprocess(  # noqa
+        o, do, w, wb, 2, 16, Hq, 2, D, BF16, None)
+    assert pre(o=None) == NULL
+    assert pre(D=48) == UNSUP
+    assert pre(Hq=3) == INVALID
+    assert pre(w=fake(2) + 64) == ALIGN
+    assert pre(wb=ws - 1) == WS
+    assert pre(w=fake(1)) == ALIAS
+    main = lambda dk=fake(5), dv=fake(6), w=fake(7), scale=0.1: L.attn_bwd_main(  # noqa
+        fake(0), fake(1), fake(2), fake(3), fake(4), dk, dv, w, ws, 2, 16, 4, 2, 64, scale, BF16, None)
+    assert main(dk=None) == NULL
+    assert main(scale=-1.0) == INVALID
+    assert main(dv=fake(5)) == ALIAS
+    assert main(w=fake(4)) == ALIAS
+    fin = lambda w=fake(0), dq=fake(1), wb=ws: L.attn_bwd_dq_finalize(  # noqa
+        w, wb, dq, 2, 16, 4, 2, 64, 0.1, BF16, None)
+    assert fin(dq=None) == NULL
+    assert fin(wb=16) == WS
+    assert fin(dq=fake(0) + 256) == ALIAS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(RuntimeError):
+        ea.rope_apply(x)
+    with pytest.raises(RuntimeError):
+        ea.attn_fwd(x, x[:, :, :1].contiguous(), x[:, :, :1].contiguous())
