@@ -2,7 +2,7 @@
 """Benchmark of libeuler_attn: one step = the whole causal-GQA-attention hot path on one
 batch of seeded synthetic inputs already resident in HBM:
 
-    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, main, dQ finalize) -> RoPE^-1(dQ), RoPE^-1(dK)
+    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, dK/dV, dQ) -> RoPE^-1(dQ), RoPE^-1(dK)
 
 Throughput is reported as TFLOP/s at the exact causal FLOP count 14 * D * B * Hq * T(T+1)/2
 (4D forward + 10D backward per unmasked query/key pair) and as a fraction of the MI355X
@@ -32,7 +32,8 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
     "attn_fwd": ["causal_gqa_attention_fwd_amd/csrc/attn_fwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
-    "attn_bwd_main": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_bwd_dkdv": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_bwd_dq": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
 }
 
 
@@ -83,11 +84,11 @@ class Step:
                                       Hkv, D, scale, dtc, stream)),
             ("attn_bwd_pre", L.attn_bwd_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq, Hkv,
                                                      D, dtc, stream)),
-            ("attn_bwd_main", L.attn_bwd_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
+            ("attn_bwd_dkdv", L.attn_bwd_dkdv, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
                                                 p(self.dk), p(self.dv), p(self.ws), nws, B, T, Hq, Hkv, D,
                                                 scale, dtc, stream)),
-            ("attn_bwd_dq_finalize", L.attn_bwd_dq_finalize, (p(self.ws), nws, p(self.dq), B, T, Hq, Hkv, D,
-                                                              scale, dtc, stream)),
+            ("attn_bwd_dq", L.attn_bwd_dq, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
+                                            p(self.dq), p(self.ws), nws, B, T, Hq, Hkv, D, scale, dtc, stream)),
             ("rope_inv_dq", L.rope_apply, (p(self.dq), p(self.dq_raw), B, T, Hq, D, dtc, base, 0, 1, stream)),
             ("rope_inv_dk", L.rope_apply, (p(self.dk), p(self.dk_raw), B, T, Hkv, D, dtc, base, 0, 1, stream)),
         ]
@@ -116,10 +117,13 @@ def algorithmic(w) -> dict:
     return {
         "rope_q": {"bytes": 2 * qb}, "rope_k": {"bytes": 2 * kb},
         "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
-        "attn_bwd_pre": {"bytes": 2 * qb + lse + w.B * w.T * w.Hq * w.D * 4},
-        "attn_bwd_main": {"flops": w.flops_bwd(), "bytes": 2 * qb + 2 * kb + 2 * lse + 2 * kb
-                          + w.B * w.T * w.Hq * w.D * 4},
-        "attn_bwd_dq_finalize": {"bytes": w.B * w.T * w.Hq * w.D * 4 + qb},
+        "attn_bwd_pre": {"bytes": 2 * qb + lse},
+        # The backward's 10D per pair: S recompute, dP, dV, dK (8D) in the dK/dV kernel, the dQ
+        # product (2D) in the dQ kernel, which also recomputes S and dP (4D executed, not
+        # counted as algorithmic work).
+        "attn_bwd_dkdv": {"flops": 8 * w.D * w.pairs, "bytes": 2 * qb + 2 * kb + 2 * lse + 2 * kb},
+        "attn_bwd_dq": {"flops": 2 * w.D * w.pairs, "executed_flops": 6 * w.D * w.pairs,
+                        "bytes": 2 * qb + 2 * kb + 2 * lse + qb},
         "rope_inv_dq": {"bytes": 2 * qb}, "rope_inv_dk": {"bytes": 2 * kb},
     }
 
@@ -177,10 +181,14 @@ def roofline_for(w, kern_us, name):
     if "flops" in alg:
         achieved = alg["flops"] / dur_s / 1e12
         peak = PEAK_TFLOPS[w.dtype]
-        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": alg["flops"], "algorithmic_bytes_per_launch": alg["bytes"],
-                "avg_launch_us": round(kern_us[name], 2)}
+        out = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+               "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+               "algorithmic_flops_per_launch": alg["flops"], "algorithmic_bytes_per_launch": alg["bytes"],
+               "avg_launch_us": round(kern_us[name], 2)}
+        if "executed_flops" in alg:
+            out["executed_flops_per_launch"] = alg["executed_flops"]
+            out["executed_tflops"] = round(alg["executed_flops"] / dur_s / 1e12, 2)
+        return out
     achieved = alg["bytes"] / dur_s / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
@@ -260,7 +268,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), causal=True,
-                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_main,attn_bwd_dq_finalize,"
+                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_dkdv,attn_bwd_dq,"
                             "rope_inv_dq,rope_inv_dk"),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": w.flops_total(),
@@ -269,6 +277,8 @@ def main() -> int:
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline_for(w, kern_us, dominant),
         "roofline_attn_fwd": roofline_for(w, kern_us, "attn_fwd"),
+        "roofline_attn_bwd_dkdv": roofline_for(w, kern_us, "attn_bwd_dkdv"),
+        "roofline_attn_bwd_dq": roofline_for(w, kern_us, "attn_bwd_dq"),
     }
     extra = {}
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:

@@ -22,7 +22,7 @@ import os
 import torch
 
 __all__ = ["rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
-           "attn_bwd_main", "attn_bwd_dq_finalize", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "attn_bwd_dkdv", "attn_bwd_dq", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
@@ -52,10 +52,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.restype = ci
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, vp]
     L.attn_bwd_preprocess.restype = ci
-    L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
-    L.attn_bwd_main.restype = ci
-    L.attn_bwd_dq_finalize.argtypes = [vp, sz, vp, ci, ci, ci, ci, ci, cf, ci, vp]
-    L.attn_bwd_dq_finalize.restype = ci
+    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_dkdv.restype = ci
+    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_dq.restype = ci
     L.euler_attn_status_string.argtypes = [ci]
     L.euler_attn_status_string.restype = ctypes.c_char_p
     L.euler_attn_version.argtypes = []
@@ -203,28 +203,27 @@ def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, workspace: torch.Te
     _raise(st, "attn_bwd_preprocess")
 
 
-def attn_bwd_main(q, k, v, lse, dout, workspace, dk, dv, scale: float | None = None) -> None:
-    """Backward stage 2: dk, dv (group-summed, overwritten) and the dQ accumulator."""
+def attn_bwd_dkdv(q, k, v, lse, dout, workspace, dk, dv, scale: float | None = None) -> None:
+    """Backward stage 2: dk, dv (group-summed, overwritten); needs the preprocess workspace."""
     B, T, Hq, Hkv, D = _shapes(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     wp, wb = _ws_args(workspace, q.device)
     with torch.cuda.device(q.device):
-        st = lib().attn_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+        st = lib().attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
                                  dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb, B, T, Hq,
                                  Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
-    _raise(st, "attn_bwd_main")
+    _raise(st, "attn_bwd_dkdv")
 
 
-def attn_bwd_dq_finalize(workspace: torch.Tensor, dq: torch.Tensor, Hkv: int,
-                         scale: float | None = None) -> None:
-    """Backward stage 3: dq = scale * accumulator, in dq's dtype."""
-    _check("dq", dq, 4)
-    B, T, Hq, D = dq.shape
+def attn_bwd_dq(q, k, v, lse, dout, workspace, dq, scale: float | None = None) -> None:
+    """Backward stage 3: dq (overwritten); needs the preprocess workspace."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    wp, wb = _ws_args(workspace, dq.device)
-    with torch.cuda.device(dq.device):
-        st = lib().attn_bwd_dq_finalize(wp, wb, dq.data_ptr(), B, T, Hq, Hkv, D, float(scale),
-                                        _dtype_code(dq), _stream(dq.device))
-    _raise(st, "attn_bwd_dq_finalize")
+    wp, wb = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                               dout.data_ptr(), dq.data_ptr(), wp, wb, B, T, Hq, Hkv, D,
+                               float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd_dq")

@@ -1,29 +1,25 @@
-// attn_bwd.hip -- causal GQA attention backward on gfx950 (attn_bwd).
+// attn_bwd.hip -- causal GQA attention backward on gfx950 (attn_bwd and its stages).
 //
 // The pages only say that NanoEuler's backward is hand-written and gradient-checked
-// ("Show HN: NanoEuler", sections 3 and 4); the algorithm here is the standard
-// recompute-from-LSE backward of tiled attention.  With P_ts = exp(S_ts - LSE_t),
-// dP = dO V^T, D_t = sum_d dO_t * O_t (= sum_s P_ts dP_ts), dS = P (dP - D_t):
+// ("Show HN: NanoEuler", sections 3 and 4); the algorithm here is the recompute-from-LSE
+// backward of tiled attention.  With P_ts = exp(S_ts - LSE_t), dP = dO V^T,
+// D_t = sum_d dO_t * O_t (= sum_s P_ts dP_ts) and dS = P (dP - D_t):
 //   dV_s = sum_{h in group} sum_{t>=s} P_ts dO_t
 //   dK_s = scale * sum_{h in group} sum_{t>=s} dS_ts Q_t
 //   dQ_t = scale * sum_{s<=t} dS_ts K_s
-// Three launches:
-//   1. bwd_pre:  D_t for every (b, h, t) and a zeroed fp32 dQ accumulator.
-//   2. bwd_main: one workgroup per (64-key tile j, K/V head, batch).  K_j and V_j stay in
+// Three launches, none of them with atomics, so every output is deterministic:
+//   1. bwd_pre:  D_t for every (b, h, t), into the workspace.
+//   2. bwd_dkdv: one workgroup per (64-key tile, K/V head, batch).  K and V stay in
 //      registers; the workgroup walks every head of the group and every query tile on or
-//      below the diagonal, so dK_j and dV_j are group-summed in registers and written once
-//      (deterministic).  dQ contributions are added to the fp32 accumulator with hardware
-//      float atomics.
-//   3. dq_convert: dQ = scale * accumulator, in the I/O dtype.
-//
-// gfx950 layout of bwd_main (4 waves; wave w owns keys 32*(w&1).. and queries 32*(w>>1)..
-// of the current 64 x 64 (query x key) tile):
-//   S = Q K^T and dP = dO V^T are 32x32 MFMA tiles whose lanes hold one key column and 16
-//   query rows, which is exactly the A-operand shape of dV += P^T dO and dK += dS^T Q, so P
-//   and dS go from accumulator to operand without leaving registers.  Q and dO are staged
-//   in LDS twice (row-major for S/dP, transposed in "slot" order for dV/dK); dS goes
-//   through LDS once so that dQ = dS K can take it in query-row form.
+//      below the diagonal, so dK and dV are group-summed in registers and written once.
+//   3. bwd_dq:   one workgroup per (query tile, K/V head, batch) over the G heads of the
+//      group, shaped like the forward: Q, dO, LSE and D stay in registers, K/V tiles stream
+//      through LDS shared by the group's heads, dQ is written once in the I/O dtype.
+// Splitting dQ out costs the S and dP products a second time (14D instead of 10D FLOPs per
+// query/key pair) but removes the fp32 atomic traffic of a fused kernel, which on this chip
+// costs more than the extra matrix-core work at these sizes.
 #include <cmath>
+#include <type_traits>
 
 #include "ea_common.h"
 #include "ea_kernels.h"
@@ -33,15 +29,35 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Two elements of T packed for one LDS store (bf16: one dword; fp32: two dwords).
+template <typename T>
+struct Pair;
+template <>
+struct Pair<bf16> {
+    typedef uint32_t type;
+    __device__ static inline uint32_t make(bf16 a, bf16 b) {
+        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+};
+template <>
+struct Pair<float> {
+    typedef float __attribute__((ext_vector_type(2))) type;
+    __device__ static inline type make(float a, float b) { return type{a, b}; }
+};
+
+template <typename T>
+__device__ inline void st_pair(T* p, T a, T b) {
+    *reinterpret_cast<typename Pair<T>::type*>(p) = Pair<T>::make(a, b);
+}
+
 // ---------------------------------------------------------------------------------------
-// 1. D_t = sum_d dO * O per row, and zero the dQ accumulator.
+// 1. D_t = sum_d dO * O per row.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
                                                       const T* __restrict__ dout,
-                                                      float* __restrict__ dt,
-                                                      float* __restrict__ dqacc, long long nrows,
-                                                      long long nacc4, int T_, int Hq) {
+                                                      float* __restrict__ dt, long long nrows,
+                                                      int T_, int Hq) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int LPR = D / EPC;  // lanes per row (4 .. 32)
     const int tid = threadIdx.x;
@@ -63,40 +79,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
         const long long b = bt / T_;
         dt[(b * Hq + h) * T_ + t] = acc;
     }
-    const long long gid = (long long)blockIdx.x * 256 + tid;
-    const long long nth = (long long)gridDim.x * 256;
-    f32x4* acc4 = reinterpret_cast<f32x4*>(dqacc);
-    for (long long i = gid; i < nacc4; i += nth) acc4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// ---------------------------------------------------------------------------------------
-// 3. dQ = scale * accumulator.
-// ---------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
-                                                         T* __restrict__ dq, long long n8,
-                                                         float scale) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a0 = reinterpret_cast<const f32x4*>(acc)[2 * i];
-    const f32x4 a1 = reinterpret_cast<const f32x4*>(acc)[2 * i + 1];
-    if constexpr (sizeof(T) == 2) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = (bf16)(a0[e] * scale);
-            v[4 + e] = (bf16)(a1[e] * scale);
-        }
-        reinterpret_cast<bf16x8*>(dq)[i] = v;
-    } else {
-        reinterpret_cast<f32x4*>(dq)[2 * i] = a0 * scale;
-        reinterpret_cast<f32x4*>(dq)[2 * i + 1] = a1 * scale;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// 2. Main backward kernel.
-// ---------------------------------------------------------------------------------------
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -104,18 +88,22 @@ struct BwdArgs {
     const void* dout;
     const float* lse;
     const float* dt;
-    float* dqacc;
+    void* dq;
     void* dk;
     void* dv;
     int B, T, Hq, Hkv;
-    int ntk;  // key tiles
-    int ntq;  // query tiles
-    float sl2;    // scale * log2(e)
+    int G, WPH, nhc;  // dq kernel: heads per workgroup, waves per head, head chunks
+    int ntk;          // key tiles
+    int ntq;          // query tiles
+    float sl2;        // scale * log2(e)
     float scale;
 };
 
+// ---------------------------------------------------------------------------------------
+// 2. dK, dV: KV-stationary.
+// ---------------------------------------------------------------------------------------
 template <typename T, int D, int BM>
-struct BwdCfg {
+struct DkdvCfg {
     static constexpr int KPL = Mfma<T>::KPL;
     static constexpr int BN = 64;               // keys per workgroup
     static constexpr int NKH = BN / 32;         // key halves
@@ -125,49 +113,34 @@ struct BwdCfg {
     static constexpr int NS = D / (2 * KPL);    // MFMA steps over head_dim
     static constexpr int NDB = D / 32;
     static constexpr int PS = 16 / KPL;         // MFMA steps over a 32-row accumulator
-    static constexpr int NSK = BN / (2 * KPL);  // MFMA steps over the tile's keys (dQ)
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;
     static constexpr int QS = D + EPC;          // row-major Q / dO stride
     static constexpr int QTS = BM + EPC;        // transposed Q / dO stride
-    static constexpr int KTS = BN + EPC;        // transposed K stride
-    static constexpr int DSS = BN + EPC;        // dS stride
-    static constexpr int NCHQ = (BM * CPR + NT - 1) / NT;
-    static constexpr int NCHK = (BN * CPR + NT - 1) / NT;
-    // LDS carve-up (bytes).
+    static constexpr int NPU = ((BM / 2) * CPR + NT - 1) / NT;  // row-pair units per thread
+    // LDS carve-up of one stage (bytes); two stages.
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_DO = OFF_Q + sizeof(T) * BM * QS;
     static constexpr size_t OFF_QT = OFF_DO + sizeof(T) * BM * QS;
     static constexpr size_t OFF_DOT = OFF_QT + sizeof(T) * D * QTS;
-    static constexpr size_t OFF_KT = OFF_DOT + sizeof(T) * D * QTS;
-    static constexpr size_t OFF_DS = OFF_KT + sizeof(T) * D * KTS;
-    static constexpr size_t OFF_LSE = OFF_DS + sizeof(T) * BM * DSS;
+    static constexpr size_t OFF_LSE = OFF_DOT + sizeof(T) * D * QTS;
     static constexpr size_t OFF_DT = OFF_LSE + sizeof(float) * BM;
-    static constexpr size_t BYTES = OFF_DT + sizeof(float) * BM;
-    // dK/dV partials of the waves with query block > 0, reduced at the end (reuses the
-    // Q / dO / Q^T / dO^T region).
+    static constexpr size_t STAGE = (OFF_DT + sizeof(float) * BM + 15) & ~(size_t)15;
+    static constexpr size_t BYTES = 2 * STAGE;
     static constexpr size_t RED_BYTES = (size_t)(NQH - 1) * NKH * 2 * NDB * 16 * 64 * sizeof(float);
-    static_assert(RED_BYTES <= OFF_KT, "reduction buffer must fit in the staging region");
+    static_assert(RED_BYTES <= BYTES, "reduction buffer must fit in the staging region");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <typename T, int D, int BM>
-__global__ __launch_bounds__((64 * BwdCfg<T, D, BM>::NW)) void attn_bwd_kernel(BwdArgs a) {
-    using C = BwdCfg<T, D, BM>;
+__global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(BwdArgs a) {
+    using C = DkdvCfg<T, D, BM>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
     constexpr int BN = C::BN;
 
     __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
-    T* Qs = reinterpret_cast<T*>(smem + C::OFF_Q);
-    T* dOs = reinterpret_cast<T*>(smem + C::OFF_DO);
-    T* QTs = reinterpret_cast<T*>(smem + C::OFF_QT);
-    T* dOTs = reinterpret_cast<T*>(smem + C::OFF_DOT);
-    T* KTs = reinterpret_cast<T*>(smem + C::OFF_KT);
-    T* dSs = reinterpret_cast<T*>(smem + C::OFF_DS);
-    float* lse2s = reinterpret_cast<float*>(smem + C::OFF_LSE);
-    float* dts = reinterpret_cast<float*>(smem + C::OFF_DT);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -206,21 +179,6 @@ __global__ __launch_bounds__((64 * BwdCfg<T, D, BM>::NW)) void attn_bwd_kernel(B
             }
         }
     }
-    // K_j^T in LDS (identity key order) for dQ = dS K.
-#pragma unroll
-    for (int n = 0; n < C::NCHK; ++n) {
-        const int c = tid + n * C::NT;
-        if (c < BN * C::CPR) {
-            const int key = c / C::CPR;
-            const int part = c % C::CPR;
-            const int s = j * BN + key;
-            const Vec16<T> kv = (s < a.T)
-                ? ld16(kp + (((long long)b * a.T + s) * a.Hkv + kvh) * D + part * C::EPC)
-                : zero16<T>();
-#pragma unroll
-            for (int e = 0; e < C::EPC; ++e) KTs[(part * C::EPC + e) * C::KTS + key] = kv.get(e);
-        }
-    }
 
     f32x16 dkacc[C::NDB], dvacc[C::NDB];
 #pragma unroll
@@ -229,98 +187,142 @@ __global__ __launch_bounds__((64 * BwdCfg<T, D, BM>::NW)) void attn_bwd_kernel(B
         dvacc[db] = zero_acc();
     }
 
+    // Iterations: every head of the group x every query tile on or below the diagonal.
     const int i0 = (j * BN) / BM;
-    for (int hs = 0; hs < g; ++hs) {
-        const int head = kvh * g + hs;
-        const float* lse_row = a.lse + ((long long)b * a.Hq + head) * a.T;
-        const float* dt_row = a.dt + ((long long)b * a.Hq + head) * a.T;
-        for (int i = i0; i < a.ntq; ++i) {
-            __syncthreads();  // previous iteration is done with the staging buffers
-            // Stage Q_i and dO_i: row-major and transposed ("slot" order per 32 rows).
+    const int nq = a.ntq - i0;
+    const int niter = g * nq;
+
+    // Staging of Q_i / dO_i (row pairs), LSE and D: HBM -> registers -> LDS.
+    Vec16<T> qreg[C::NPU][2], dreg[C::NPU][2];
+    float lreg = 0.0f, treg = 0.0f;
+    auto fetch = [&](int it) {
+        const int head = kvh * g + it / nq;
+        const int i = i0 + it % nq;
 #pragma unroll
-            for (int n = 0; n < C::NCHQ; ++n) {
-                const int c = tid + n * C::NT;
-                if (c < BM * C::CPR) {
-                    const int qr = c / C::CPR;
-                    const int part = c % C::CPR;
-                    const int t = i * BM + qr;
-                    Vec16<T> qv = zero16<T>(), dv = zero16<T>();
+        for (int n = 0; n < C::NPU; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BM / 2) * C::CPR) {
+                const int rp = u % (BM / 2), part = u / (BM / 2);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int t = i * BM + 2 * rp + e;
                     if (t < a.T) {
                         const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC;
-                        qv = ld16(qp + off);
-                        dv = ld16(dop + off);
+                        qreg[n][e] = ld16(qp + off);
+                        dreg[n][e] = ld16(dop + off);
+                    } else {
+                        qreg[n][e] = zero16<T>();
+                        dreg[n][e] = zero16<T>();
                     }
-                    st16(&Qs[qr * C::QS + part * C::EPC], qv);
-                    st16(&dOs[qr * C::QS + part * C::EPC], dv);
-                    const int slot = (qr & ~31) + acc_slot(qr & 31);
-#pragma unroll
-                    for (int e = 0; e < C::EPC; ++e) {
-                        QTs[(part * C::EPC + e) * C::QTS + slot] = qv.get(e);
-                        dOTs[(part * C::EPC + e) * C::QTS + slot] = dv.get(e);
-                    }
-                }
-            }
-            for (int qr = tid; qr < BM; qr += C::NT) {
-                const int t = i * BM + qr;
-                lse2s[qr] = (t < a.T) ? lse_row[t] * kLog2e : INFINITY;
-                dts[qr] = (t < a.T) ? dt_row[t] : 0.0f;
-            }
-            __syncthreads();
-
-            // S = Q K^T and dP = dO V^T on this wave's 32 x 32 block.
-            f32x16 sacc = zero_acc(), dpacc = zero_acc();
-#pragma unroll
-            for (int s = 0; s < C::NS; ++s) {
-                const int ro = (qh * 32 + l32) * C::QS + half * (D / 2) + s * KPL;
-                sacc = M::mma(load_frag<T>(&Qs[ro]), kf[s], sacc);
-                dpacc = M::mma(load_frag<T>(&dOs[ro]), vf[s], dpacc);
-            }
-            // P = exp(S - LSE), masked on blocks crossing the diagonal; dS = P (dP - D).
-            const bool diag = (j * BN + kh * 32 + 31) > (i * BM + qh * 32);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int lq = qh * 32 + acc_row(r, half);
-                float p = __builtin_amdgcn_exp2f(sacc[r] * a.sl2 - lse2s[lq]);
-                if (diag && mykey > i * BM + lq) p = 0.0f;
-                sacc[r] = p;
-                dpacc[r] = p * (dpacc[r] - dts[lq]);
-            }
-            // dV += P^T dO and dK += dS^T Q (contraction over this wave's 32 queries).
-#pragma unroll
-            for (int ps = 0; ps < C::PS; ++ps) {
-                const frag pf = acc_to_frag<T>(sacc, ps * KPL);
-                const frag dsf = acc_to_frag<T>(dpacc, ps * KPL);
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const int ro = (db * 32 + l32) * C::QTS + qh * 32 + 16 * half + ps * KPL;
-                    dvacc[db] = M::mma(pf, load_frag<T>(&dOTs[ro]), dvacc[db]);
-                    dkacc[db] = M::mma(dsf, load_frag<T>(&QTs[ro]), dkacc[db]);
-                }
-            }
-            // dS to LDS in query-row form.
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dSs[(qh * 32 + acc_row(r, half)) * C::DSS + kh * 32 + l32] = from_f32<T>(dpacc[r]);
-            __syncthreads();
-            // dQ_i += dS K_j ("split" over the tile's keys), one 32x32 block per wave turn.
-            for (int blk = w; blk < C::NQH * C::NDB; blk += C::NW) {
-                const int qb = blk / C::NDB;
-                const int db = blk % C::NDB;
-                f32x16 acc = zero_acc();
-#pragma unroll
-                for (int s = 0; s < C::NSK; ++s) {
-                    const frag af = load_frag<T>(&dSs[(qb * 32 + l32) * C::DSS + half * (BN / 2) + s * KPL]);
-                    const frag bk = load_frag<T>(&KTs[(db * 32 + l32) * C::KTS + half * (BN / 2) + s * KPL]);
-                    acc = M::mma(af, bk, acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = i * BM + qb * 32 + acc_row(r, half);
-                    if (t < a.T)
-                        unsafeAtomicAdd(&a.dqacc[(((long long)b * a.T + t) * a.Hq + head) * D + db * 32 + l32], acc[r]);
                 }
             }
         }
+        if (tid < BM) {
+            const int t = i * BM + tid;
+            const long long ro = ((long long)b * a.Hq + head) * a.T;
+            lreg = (t < a.T) ? a.lse[ro + t] * kLog2e : INFINITY;
+            treg = (t < a.T) ? a.dt[ro + t] : 0.0f;
+        }
+    };
+    auto commit = [&](int stage) {
+        char* base = smem + stage * C::STAGE;
+        T* Qs = reinterpret_cast<T*>(base + C::OFF_Q);
+        T* dOs = reinterpret_cast<T*>(base + C::OFF_DO);
+        T* QTs = reinterpret_cast<T*>(base + C::OFF_QT);
+        T* dOTs = reinterpret_cast<T*>(base + C::OFF_DOT);
+#pragma unroll
+        for (int n = 0; n < C::NPU; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BM / 2) * C::CPR) {
+                const int rp = u % (BM / 2), part = u / (BM / 2);
+                const int r0 = 2 * rp;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    st16(&Qs[(r0 + e) * C::QS + part * C::EPC], qreg[n][e]);
+                    st16(&dOs[(r0 + e) * C::QS + part * C::EPC], dreg[n][e]);
+                }
+                const int slot = (r0 & ~31) + acc_slot(r0 & 31);  // slot(r0 + 1) == slot + 1
+#pragma unroll
+                for (int e = 0; e < C::EPC; ++e) {
+                    const int d = part * C::EPC + e;
+                    st_pair<T>(&QTs[d * C::QTS + slot], qreg[n][0].get(e), qreg[n][1].get(e));
+                    st_pair<T>(&dOTs[d * C::QTS + slot], dreg[n][0].get(e), dreg[n][1].get(e));
+                }
+            }
+        }
+        if (tid < BM) {
+            reinterpret_cast<float*>(base + C::OFF_LSE)[tid] = lreg;
+            reinterpret_cast<float*>(base + C::OFF_DT)[tid] = treg;
+        }
+    };
+
+    auto compute = [&](int it, int stage, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        const int i = i0 + it % nq;
+        const char* base = smem + stage * C::STAGE;
+        const T* Qs = reinterpret_cast<const T*>(base + C::OFF_Q);
+        const T* dOs = reinterpret_cast<const T*>(base + C::OFF_DO);
+        const T* QTs = reinterpret_cast<const T*>(base + C::OFF_QT);
+        const T* dOTs = reinterpret_cast<const T*>(base + C::OFF_DOT);
+        const float* lse2s = reinterpret_cast<const float*>(base + C::OFF_LSE);
+        const float* dts = reinterpret_cast<const float*>(base + C::OFF_DT);
+        // S = Q K^T and dP = dO V^T on this wave's 32 x 32 block (lanes = keys).
+        f32x16 sacc = zero_acc(), dpacc = zero_acc();
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const int ro = (qh * 32 + l32) * C::QS + half * (D / 2) + s * KPL;
+            sacc = M::mma(load_frag<T>(&Qs[ro]), kf[s], sacc);
+            dpacc = M::mma(load_frag<T>(&dOs[ro]), vf[s], dpacc);
+        }
+        // P = exp(S - LSE) (masked where key > query); dS = P (dP - D).
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int lq0 = qh * 32 + 8 * r4 + 4 * half;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[lq0]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int r = 4 * r4 + c;
+                float p = __builtin_amdgcn_exp2f(sacc[r] * a.sl2 - l4[c]);
+                if constexpr (MASK) {
+                    if (mykey > i * BM + lq0 + c) p = 0.0f;
+                }
+                sacc[r] = p;
+                dpacc[r] = p * (dpacc[r] - d4[c]);
+            }
+        }
+        // dV += P^T dO and dK += dS^T Q (contraction over this wave's 32 queries).
+#pragma unroll
+        for (int ps = 0; ps < C::PS; ++ps) {
+            const frag pf = acc_to_frag<T>(sacc, ps * KPL);
+            const frag dsf = acc_to_frag<T>(dpacc, ps * KPL);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const int ro = (db * 32 + l32) * C::QTS + qh * 32 + 16 * half + ps * KPL;
+                dvacc[db] = M::mma(pf, load_frag<T>(&dOTs[ro]), dvacc[db]);
+                dkacc[db] = M::mma(dsf, load_frag<T>(&QTs[ro]), dkacc[db]);
+            }
+        }
+    };
+
+    if (niter > 0) {
+        fetch(0);
+        commit(0);
+        if (niter > 1) fetch(1);
+    }
+    for (int it = 0; it < niter; ++it) {
+        __syncthreads();  // stage it&1 visible; stage (it+1)&1 free
+        if (it + 1 < niter) {
+            commit((it + 1) & 1);
+            if (it + 2 < niter) fetch(it + 2);
+        }
+        const int i = i0 + it % nq;
+        // Mask when the wave's key block reaches past its query block's first row.
+        const bool diag = (j * BN + kh * 32 + 31) > (i * BM + qh * 32);
+        if (diag)
+            compute(it, it & 1, std::true_type{});
+        else
+            compute(it, it & 1, std::false_type{});
     }
 
     // Reduce the dK/dV partials of the query blocks and store (dK scaled by `scale`).
@@ -364,81 +366,319 @@ __global__ __launch_bounds__((64 * BwdCfg<T, D, BM>::NW)) void attn_bwd_kernel(B
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// 3. dQ: Q-stationary, shaped like the forward.
+// ---------------------------------------------------------------------------------------
+template <typename T, int D, int BN, int NW>
+struct DqCfg {
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int NS = D / (2 * KPL);
+    static constexpr int NKB = BN / 32;
+    static constexpr int NDB = D / 32;
+    static constexpr int PS = 16 / KPL;
+    static constexpr int EPC = 16 / sizeof(T);
+    static constexpr int CPR = D / EPC;
+    static constexpr int KS = D + EPC;   // row-major K / V stride
+    static constexpr int TS = BN + EPC;  // transposed K stride
+    static constexpr int NT = 64 * NW;
+    static constexpr int NPU = ((BN / 2) * CPR + NT - 1) / NT;  // key-pair units per thread
+    static constexpr int KBUF = BN * KS;
+    static constexpr int TBUF = D * TS;
+    static constexpr int STAGE = 2 * KBUF + TBUF;  // K, V row-major; K^T
+};
+
+template <typename T, int D, int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+    using C = DqCfg<T, D, BN, NW>;
+    using M = Mfma<T>;
+    using frag = typename M::frag;
+    constexpr int KPL = C::KPL;
+
+    __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    const int HB = a.B * a.Hkv * a.nhc;
+    const int L = blockIdx.x;
+    const int tile = a.ntq - 1 - L / HB;
+    const int rem = L % HB;
+    const int hc = rem % a.nhc;
+    const int kvh = (rem / a.nhc) % a.Hkv;
+    const int b = rem / (a.nhc * a.Hkv);
+    const int g = a.Hq / a.Hkv;
+    const int BM = a.WPH * 32;
+    const int hs = w / a.WPH;
+    const int sub = w % a.WPH;
+    const int head = kvh * g + hc * a.G + hs;
+    const int q0 = tile * BM + sub * 32;
+    const bool active = q0 < a.T;
+    const int wg_last = min(tile * BM + BM, a.T) - 1;
+    const int jmax = wg_last / BN;
+    const int tq = q0 + l32;  // this lane's query
+
+    const T* __restrict__ qp = static_cast<const T*>(a.q);
+    const T* __restrict__ kp = static_cast<const T*>(a.k);
+    const T* __restrict__ vp = static_cast<const T*>(a.v);
+    const T* __restrict__ dop = static_cast<const T*>(a.dout);
+    const long long kv_row0 = (long long)b * a.T;
+
+    // Q and dO fragments ("split" over head_dim), LSE and D of this lane's query.
+    frag qf[C::NS], df[C::NS];
+    float lse2 = INFINITY, dtv = 0.0f;
+    if (active && tq < a.T) {
+        const long long off = (((long long)b * a.T + tq) * a.Hq + head) * D + half * (D / 2);
+#pragma unroll
+        for (int c = 0; c < (D / 2) / C::EPC; ++c) {
+            const Vec16<T> qv = ld16(qp + off + c * C::EPC);
+            const Vec16<T> dv = ld16(dop + off + c * C::EPC);
+#pragma unroll
+            for (int e = 0; e < C::EPC / KPL; ++e) {
+                qf[c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&qv.raw)[e];
+                df[c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&dv.raw)[e];
+            }
+        }
+        const long long ro = ((long long)b * a.Hq + head) * a.T + tq;
+        lse2 = a.lse[ro] * kLog2e;
+        dtv = a.dt[ro];
+    } else {
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            qf[s] = frag{};
+            df[s] = frag{};
+        }
+    }
+
+    // Staging of one K/V tile (pairs of key rows): K and V row-major, K transposed.
+    Vec16<T> kreg[C::NPU][2], vreg[C::NPU][2];
+    auto fetch = [&](int j) {
+#pragma unroll
+        for (int n = 0; n < C::NPU; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BN / 2) * C::CPR) {
+                const int kpair = u % (BN / 2), part = u / (BN / 2);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int s = j * BN + 2 * kpair + e;
+                    if (s < a.T) {
+                        const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
+                        kreg[n][e] = ld16(kp + off);
+                        vreg[n][e] = ld16(vp + off);
+                    } else {
+                        kreg[n][e] = zero16<T>();
+                        vreg[n][e] = zero16<T>();
+                    }
+                }
+            }
+        }
+    };
+    auto commit = [&](int stage) {
+        T* Ks = smem + stage * C::STAGE;
+        T* Vs = Ks + C::KBUF;
+        T* KT = Vs + C::KBUF;
+#pragma unroll
+        for (int n = 0; n < C::NPU; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BN / 2) * C::CPR) {
+                const int kpair = u % (BN / 2), part = u / (BN / 2);
+                const int k0 = 2 * kpair;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    st16(&Ks[(k0 + e) * C::KS + part * C::EPC], kreg[n][e]);
+                    st16(&Vs[(k0 + e) * C::KS + part * C::EPC], vreg[n][e]);
+                }
+                const int slot = (k0 & ~31) + acc_slot(k0 & 31);
+#pragma unroll
+                for (int e = 0; e < C::EPC; ++e)
+                    st_pair<T>(&KT[(part * C::EPC + e) * C::TS + slot], kreg[n][0].get(e), kreg[n][1].get(e));
+            }
+        }
+    };
+
+    f32x16 dqacc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dqacc[db] = zero_acc();
+
+    auto compute = [&](int j, int stage, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        const T* Ks = smem + stage * C::STAGE;
+        const T* Vs = Ks + C::KBUF;
+        const T* KT = Vs + C::KBUF;
+        f32x16 sacc[C::NKB], pacc[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            sacc[kb] = zero_acc();
+            pacc[kb] = zero_acc();
+        }
+        // S^T = K Q^T and dP^T = V dO^T (lanes = queries, registers = keys).
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                const int ro = (kb * 32 + l32) * C::KS + half * (D / 2) + s * KPL;
+                sacc[kb] = M::mma(load_frag<T>(&Ks[ro]), qf[s], sacc[kb]);
+                pacc[kb] = M::mma(load_frag<T>(&Vs[ro]), df[s], pacc[kb]);
+            }
+        }
+        // dS^T = P^T (dP^T - D), P^T = exp(S^T - LSE).
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(sacc[kb][r] * a.sl2 - lse2);
+                if constexpr (MASK) {
+                    if (j * BN + kb * 32 + acc_row(r, half) > tq) p = 0.0f;
+                }
+                pacc[kb][r] = p * (pacc[kb][r] - dtv);
+            }
+        }
+        // dQ^T += K^T dS^T.
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int ps = 0; ps < C::PS; ++ps) {
+                const frag dsf = acc_to_frag<T>(pacc[kb], ps * KPL);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    const frag kt = load_frag<T>(&KT[(db * 32 + l32) * C::TS + kb * 32 + 16 * half + ps * KPL]);
+                    dqacc[db] = M::mma(kt, dsf, dqacc[db]);
+                }
+            }
+        }
+    };
+
+    fetch(0);
+    commit(0);
+    if (jmax >= 1) fetch(1);
+    const int qlast = min(q0 + 32, a.T) - 1;
+    const int jfirst_masked = q0 / BN;
+    for (int j = 0; j <= jmax; ++j) {
+        __syncthreads();
+        if (j + 1 <= jmax) {
+            commit((j + 1) & 1);
+            if (j + 2 <= jmax) fetch(j + 2);
+        }
+        if (!active || j * BN > qlast) continue;
+        if (j >= jfirst_masked)
+            compute(j, j & 1, std::true_type{});
+        else
+            compute(j, j & 1, std::false_type{});
+    }
+
+    if (!active || tq >= a.T) return;
+    T* __restrict__ dqp = static_cast<T*>(a.dq);
+    T* row = dqp + (((long long)b * a.T + tq) * a.Hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = db * 32 + 8 * a4 + 4 * half;
+            if constexpr (sizeof(T) == 2) {
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[db][4 * a4 + e] * a.scale);
+                *reinterpret_cast<bf16x4*>(row + d0) = v;
+            } else {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = dqacc[db][4 * a4 + e] * a.scale;
+                *reinterpret_cast<f32x4*>(row + d0) = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------------------
 template <typename T, int D>
-hipError_t launch_pre_t(const void* o, const void* dout, float* dqacc, float* dtbuf, int B, int seq,
-                        int Hq, hipStream_t stream) {
+hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, int seq, int Hq,
+                        hipStream_t stream) {
     const long long nrows = (long long)B * seq * Hq;
-    const long long nacc = nrows * D;
     constexpr int LPR = D / (16 / sizeof(T));
     const long long rows_per_block = 256 / LPR;
     const long long blocks = (nrows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const T*>(o), static_cast<const T*>(dout), dtbuf, dqacc, nrows,
-                       nacc / 4, seq, Hq);
+                       static_cast<const T*>(o), static_cast<const T*>(dout), dtbuf, nrows, seq, Hq);
     return hipGetLastError();
 }
 
 template <typename T, int D, int BM>
-hipError_t launch_main_t(const BwdArgs& a0, hipStream_t stream) {
+hipError_t launch_dkdv_t(const BwdArgs& a0, hipStream_t stream) {
     BwdArgs a = a0;
-    using C = BwdCfg<T, D, BM>;
+    using C = DkdvCfg<T, D, BM>;
     a.ntk = (a.T + C::BN - 1) / C::BN;
     a.ntq = (a.T + BM - 1) / BM;
     const long long blocks = (long long)a.ntk * a.B * a.Hkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_kernel<T, D, BM>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BM>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_convert_t(const float* dqacc, void* dq, long long nacc, float scale,
-                            hipStream_t stream) {
-    const long long n8 = nacc / 8;
-    const long long blocks = (n8 + 255) / 256;
+// Same grouping rule as the forward: G = largest divisor of g that is at most four; two
+// waves per head (four when G <= 2) for head_dim <= 64, one for head_dim 128.
+template <int D>
+void pick_dq_group(int g, int* G, int* WPH) {
+    int G_ = 1;
+    for (int c = 4; c >= 1; --c)
+        if (g % c == 0) {
+            G_ = c;
+            break;
+        }
+    *G = G_;
+    if (D >= 128)
+        *WPH = (G_ >= 3) ? 1 : 4 / G_;
+    else
+        *WPH = (G_ <= 2) ? 4 : 2;
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) {
+    BwdArgs a = a0;
+    constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // LDS budget of fp32 / D=128
+    a.G = G;
+    a.WPH = WPH;
+    a.nhc = (a.Hq / a.Hkv) / G;
+    const int BM = WPH * 32;
+    a.ntq = (a.T + BM - 1) / BM;
+    const long long blocks = (long long)a.ntq * a.B * a.Hkv * a.nhc;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, dqacc,
-                       static_cast<T*>(dq), n8, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
-float* ws_dqacc(void* ws) { return static_cast<float*>(ws); }
-
-float* ws_dt(void* ws, int B, int T, int Hq, int D) {
-    return reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)B * T * Hq * D * sizeof(float)));
-}
-
-}  // namespace
-
-size_t bwd_workspace_bytes(int B, int T, int Hq, int D) {
-    return align256((size_t)B * T * Hq * D * sizeof(float)) + align256((size_t)B * Hq * T * sizeof(float));
-}
-
-hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
-                          int D, IoType dt, hipStream_t stream) {
-    float* acc = ws_dqacc(workspace);
-    float* dtb = ws_dt(workspace, B, T, Hq, D);
-    if (dt == kF32) {
-        if (D == 32) return launch_pre_t<float, 32>(o, dout, acc, dtb, B, T, Hq, stream);
-        if (D == 64) return launch_pre_t<float, 64>(o, dout, acc, dtb, B, T, Hq, stream);
-        return launch_pre_t<float, 128>(o, dout, acc, dtb, B, T, Hq, stream);
+template <typename T, int D>
+hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
+    int G, WPH;
+    pick_dq_group<D>(a.Hq / a.Hkv, &G, &WPH);
+    const int nw = G * WPH;
+    if constexpr (D >= 128) {
+        if (nw == 3) return launch_dq_cfg<T, D, 3>(a, G, WPH, stream);
+        return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
+    } else {
+        if (nw == 6) return launch_dq_cfg<T, D, 6>(a, G, WPH, stream);
+        if (nw == 4) return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
+        return launch_dq_cfg<T, D, 8>(a, G, WPH, stream);
     }
-    if (D == 32) return launch_pre_t<bf16, 32>(o, dout, acc, dtb, B, T, Hq, stream);
-    if (D == 64) return launch_pre_t<bf16, 64>(o, dout, acc, dtb, B, T, Hq, stream);
-    return launch_pre_t<bf16, 128>(o, dout, acc, dtb, B, T, Hq, stream);
 }
 
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
-                           const void* dout, void* dk, void* dv, void* workspace, int B, int T,
-                           int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
+float* ws_dt(void* ws) { return static_cast<float*>(ws); }
+
+BwdArgs make_args(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, int B, int T, int Hq, int Hkv,
+                  float scale) {
     BwdArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
     a.dout = dout;
     a.lse = lse;
-    a.dt = ws_dt(workspace, B, T, Hq, D);
-    a.dqacc = ws_dqacc(workspace);
+    a.dt = ws_dt(workspace);
+    a.dq = dq;
     a.dk = dk;
     a.dv = dv;
     a.B = B;
@@ -447,22 +687,55 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const fl
     a.Hkv = Hkv;
     a.sl2 = scale * kLog2e;
     a.scale = scale;
-    if (dt == kF32) {
-        if (D == 32) return launch_main_t<float, 32, 64>(a, stream);
-        if (D == 64) return launch_main_t<float, 64, 64>(a, stream);
-        return launch_main_t<float, 128, 32>(a, stream);
-    }
-    if (D == 32) return launch_main_t<bf16, 32, 64>(a, stream);
-    if (D == 64) return launch_main_t<bf16, 64, 64>(a, stream);
-    return launch_main_t<bf16, 128, 64>(a, stream);
+    return a;
 }
 
-hipError_t launch_bwd_dq_finalize(const void* workspace, void* dq, int B, int T, int Hq, int D,
-                                  float scale, IoType dt, hipStream_t stream) {
-    const float* acc = static_cast<const float*>(workspace);
-    const long long nacc = (long long)B * T * Hq * D;
-    if (dt == kF32) return launch_convert_t<float>(acc, dq, nacc, scale, stream);
-    return launch_convert_t<bf16>(acc, dq, nacc, scale, stream);
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int T, int Hq, int D) {
+    (void)D;
+    return align256((size_t)B * Hq * T * sizeof(float));
+}
+
+hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
+                          int D, IoType dt, hipStream_t stream) {
+    float* dtb = ws_dt(workspace);
+    if (dt == kF32) {
+        if (D == 32) return launch_pre_t<float, 32>(o, dout, dtb, B, T, Hq, stream);
+        if (D == 64) return launch_pre_t<float, 64>(o, dout, dtb, B, T, Hq, stream);
+        return launch_pre_t<float, 128>(o, dout, dtb, B, T, Hq, stream);
+    }
+    if (D == 32) return launch_pre_t<bf16, 32>(o, dout, dtb, B, T, Hq, stream);
+    if (D == 64) return launch_pre_t<bf16, 64>(o, dout, dtb, B, T, Hq, stream);
+    return launch_pre_t<bf16, 128>(o, dout, dtb, B, T, Hq, stream);
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, void* dk, void* dv, void* workspace, int B, int T,
+                           int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
+    const BwdArgs a = make_args(q, k, v, lse, dout, nullptr, dk, dv, workspace, B, T, Hq, Hkv, scale);
+    if (dt == kF32) {
+        if (D == 32) return launch_dkdv_t<float, 32, 64>(a, stream);
+        if (D == 64) return launch_dkdv_t<float, 64, 64>(a, stream);
+        return launch_dkdv_t<float, 128, 32>(a, stream);
+    }
+    if (D == 32) return launch_dkdv_t<bf16, 32, 64>(a, stream);
+    if (D == 64) return launch_dkdv_t<bf16, 64, 64>(a, stream);
+    return launch_dkdv_t<bf16, 128, 64>(a, stream);
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, void* dq, void* workspace, int B, int T, int Hq,
+                         int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
+    const BwdArgs a = make_args(q, k, v, lse, dout, dq, nullptr, nullptr, workspace, B, T, Hq, Hkv, scale);
+    if (dt == kF32) {
+        if (D == 32) return launch_dq_t<float, 32>(a, stream);
+        if (D == 64) return launch_dq_t<float, 64>(a, stream);
+        return launch_dq_t<float, 128>(a, stream);
+    }
+    if (D == 32) return launch_dq_t<bf16, 32>(a, stream);
+    if (D == 64) return launch_dq_t<bf16, 64>(a, stream);
+    return launch_dq_t<bf16, 128>(a, stream);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -471,9 +744,9 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            IoType dt, hipStream_t stream) {
     hipError_t e = launch_bwd_pre(o, dout, workspace, B, T, Hq, D, dt, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_main(q, k, v, lse, dout, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
+    e = launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_finalize(workspace, dq, B, T, Hq, D, scale, dt, stream);
+    return launch_bwd_dq(q, k, v, lse, dout, dq, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
 }
 
 }  // namespace ea

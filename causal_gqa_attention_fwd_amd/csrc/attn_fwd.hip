@@ -5,27 +5,31 @@
 // section 1: causal scaled dot-product attention; "Show HN: NanoEuler", section 2: query
 // heads share K/V heads).  As the NanoEuler engine does ("Show HN: NanoEuler", section 4;
 // the blog's "Tiled FlashAttention" section), keys are consumed tile by tile with an online
-// softmax (running max m, running sum l, rescale of the partial output by 2^(m_old-m_new)),
-// so no T x T matrix exists anywhere.
+// softmax (running max, running sum, rescale of the partial output), so no T x T matrix
+// exists anywhere.
 //
 // gfx950 design:
-//  * One workgroup = one query tile of one batch and G heads of one K/V head group (G
-//    waves, or G * WPH waves when a head gets several waves).  Each K/V tile is read from
-//    HBM once into LDS and shared by every head of the group.
-//  * Each wave owns 32*QB query rows of one head and keeps them, their output accumulator
-//    and their softmax state in registers.  Scores are formed transposed, S^T = K Q^T, on
-//    32x32 MFMA tiles: a lane then holds one query column and 16 keys per tile, so the
-//    row max and row sum are in-lane reductions plus one exchange between the two lane
-//    halves.  O^T += V^T P^T reuses the score registers directly as the B operand.
-//  * K is staged row-major (A operand of S^T, read as 16-byte runs); V is staged
-//    transposed and in "slot" order (A operand of O^T).  LDS rows carry 16 bytes of
-//    padding so that 16 lanes of a 16-byte read hit distinct banks.
-//  * The next K/V tile is fetched from HBM into registers (16-byte coalesced loads)
-//    while the current tile is computed.
-//  * Tiles strictly above the diagonal are never visited; the mask is evaluated only on
-//    tiles that cross the diagonal.  The launch order puts the longest (latest) query
-//    tiles first, and workgroups of one K/V head land on the same XCD for L2 reuse.
+//  * One workgroup = one query tile of one batch and the G heads of one K/V head group
+//    (G * WPH waves, WPH waves per head).  Each K/V tile is read from HBM once into LDS and
+//    shared by every head of the group.
+//  * Each wave owns 32*QB query rows of one head: their Q fragments, output accumulator and
+//    softmax state stay in registers.  Scores are formed transposed, S^T = K Q^T, on 32x32
+//    MFMA tiles: a lane then holds one query column and 16 keys per tile, so the row max and
+//    row sum are in-lane reductions plus one exchange between the two lane halves.
+//    O^T += V^T P^T takes the score registers directly as its B operand.
+//  * K is staged row-major (A operand of S^T); V is staged transposed in "slot" order
+//    (A operand of O^T), written as packed pairs of keys so a wave's LDS stores hit 64
+//    distinct banks.  Rows carry 16 bytes of padding so 16-byte operand reads are
+//    conflict-free.  Two LDS buffers: tile j+1 is committed from registers while tile j is
+//    computed, and tile j+2 is in flight from HBM; one barrier per tile.
+//  * The online-softmax rescale is lazy: the running max used for exponentiation is raised
+//    only when a row's max grows by more than 2^8 (then O and l are rescaled), so P stays
+//    below 256 and most tiles skip the rescale; the result is exact either way.
+//  * Tiles strictly above the diagonal are never visited; the causal mask is evaluated only
+//    on the one tile that crosses a wave's diagonal.  The launch order puts the longest
+//    (latest) query tiles first; workgroups of one K/V head land on the same XCD.
 #include <cmath>
+#include <type_traits>
 
 #include "ea_common.h"
 #include "ea_kernels.h"
@@ -47,6 +51,8 @@ struct FwdArgs {
     float sl2;  // scale * log2(e)
 };
 
+constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest un-normalised P
+
 template <typename T, int D, int QB, int BN, int NW>
 struct FwdCfg {
     static constexpr int KPL = Mfma<T>::KPL;
@@ -59,8 +65,27 @@ struct FwdCfg {
     static constexpr int KS = D + EPC;        // K tile row stride (16 bytes of padding)
     static constexpr int VS = BN + EPC;       // V^T tile row stride
     static constexpr int NT = 64 * NW;
-    static constexpr int NCH = (BN * CPR + NT - 1) / NT;
+    static constexpr int NCHK = (BN * CPR + NT - 1) / NT;        // K chunks per thread
+    static constexpr int NCHV = ((BN / 2) * CPR + NT - 1) / NT;  // V chunk pairs per thread
     static constexpr int QW = 32 * QB;
+    static constexpr int KBUF = BN * KS;
+    static constexpr int VBUF = D * VS;
+};
+
+// Two elements of T packed for one LDS store (bf16: one dword; fp32: two dwords).
+template <typename T>
+struct Pair;
+template <>
+struct Pair<bf16> {
+    typedef uint32_t type;
+    __device__ static inline uint32_t make(bf16 a, bf16 b) {
+        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+};
+template <>
+struct Pair<float> {
+    typedef float __attribute__((ext_vector_type(2))) type;
+    __device__ static inline type make(float a, float b) { return type{a, b}; }
 };
 
 template <typename T, int D, int QB, int BN, int NW>
@@ -70,8 +95,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
 
-    __shared__ __attribute__((aligned(16))) T Ks[BN * C::KS];
-    __shared__ __attribute__((aligned(16))) T Vt[D * C::VS];
+    __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
+    __shared__ __attribute__((aligned(16))) T Vt[2 * C::VBUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,6 +125,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     const T* __restrict__ qp = static_cast<const T*>(a.q);
     const T* __restrict__ kp = static_cast<const T*>(a.k);
     const T* __restrict__ vp = static_cast<const T*>(a.v);
+    const long long kv_row0 = (long long)b * a.T;  // row index of key 0 of this batch
 
     // Q fragments ("split" over head_dim): lane (query l32, half) holds half*D/2 .. +D/2.
     frag qf[QB][C::NS];
@@ -112,10 +138,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
             for (int c = 0; c < (D / 2) / C::EPC; ++c) {
                 Vec16<T> v = ld16(row + c * C::EPC);
 #pragma unroll
-                for (int e = 0; e < C::EPC / KPL; ++e) {
-                    qf[qb][c * (C::EPC / KPL) + e] =
-                        reinterpret_cast<const frag*>(&v.raw)[e];
-                }
+                for (int e = 0; e < C::EPC / KPL; ++e)
+                    qf[qb][c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&v.raw)[e];
             }
         } else {
 #pragma unroll
@@ -123,134 +147,165 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
     }
 
-    Vec16<T> kreg[C::NCH], vreg[C::NCH];
+    // Staging of one K/V tile: HBM -> registers (fetch) -> LDS (commit).
+    Vec16<T> kreg[C::NCHK], vreg[C::NCHV][2];
     auto fetch = [&](int j) {
 #pragma unroll
-        for (int n = 0; n < C::NCH; ++n) {
+        for (int n = 0; n < C::NCHK; ++n) {
             const int c = tid + n * C::NT;
             if (c < BN * C::CPR) {
-                const int key = c / C::CPR;
-                const int part = c % C::CPR;
+                const int key = c / C::CPR, part = c % C::CPR;
                 const int s = j * BN + key;
-                if (s < a.T) {
-                    const long long off =
-                        (((long long)b * a.T + s) * a.Hkv + kvh) * D + part * C::EPC;
-                    kreg[n] = ld16(kp + off);
-                    vreg[n] = ld16(vp + off);
-                } else {
-                    kreg[n] = zero16<T>();
-                    vreg[n] = zero16<T>();
+                kreg[n] = (s < a.T) ? ld16(kp + ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC)
+                                    : zero16<T>();
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < C::NCHV; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BN / 2) * C::CPR) {
+                const int kpair = u % (BN / 2), part = u / (BN / 2);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int s = j * BN + 2 * kpair + e;
+                    vreg[n][e] = (s < a.T)
+                        ? ld16(vp + ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC)
+                        : zero16<T>();
                 }
             }
         }
     };
-    auto commit = [&]() {
+    auto commit = [&](int buf) {
+        T* kb = Ks + buf * C::KBUF;
+        T* vb = Vt + buf * C::VBUF;
 #pragma unroll
-        for (int n = 0; n < C::NCH; ++n) {
+        for (int n = 0; n < C::NCHK; ++n) {
             const int c = tid + n * C::NT;
             if (c < BN * C::CPR) {
-                const int key = c / C::CPR;
-                const int part = c % C::CPR;
-                st16(&Ks[key * C::KS + part * C::EPC], kreg[n]);
-                const int slot = (key & ~31) + acc_slot(key & 31);
+                const int key = c / C::CPR, part = c % C::CPR;
+                st16(&kb[key * C::KS + part * C::EPC], kreg[n]);
+            }
+        }
 #pragma unroll
-                for (int e = 0; e < C::EPC; ++e) Vt[(part * C::EPC + e) * C::VS + slot] = vreg[n].get(e);
+        for (int n = 0; n < C::NCHV; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < (BN / 2) * C::CPR) {
+                const int kpair = u % (BN / 2), part = u / (BN / 2);
+                const int key = 2 * kpair;
+                const int slot = (key & ~31) + acc_slot(key & 31);  // slot(key + 1) == slot + 1
+#pragma unroll
+                for (int e = 0; e < C::EPC; ++e) {
+                    *reinterpret_cast<typename Pair<T>::type*>(&vb[(part * C::EPC + e) * C::VS + slot]) =
+                        Pair<T>::make(vreg[n][0].get(e), vreg[n][1].get(e));
+                }
             }
         }
     };
 
-    float m[QB], l[QB];
+    float mrun[QB], l[QB];
     f32x16 oacc[QB][C::NDB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
+        mrun[qb] = -INFINITY;
         l[qb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) oacc[qb][db] = zero_acc();
     }
 
-    fetch(0);
-    for (int j = 0; j <= jmax; ++j) {
-        __syncthreads();
-        commit();
-        __syncthreads();
-        if (j < jmax) fetch(j + 1);
-        if (!active || j * BN > qlast) continue;
-        const bool diag = (j * BN + BN - 1) > q0;
-
-        // S^T = K Q^T for this tile.
+    // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto compute = [&](int j, int buf, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        const T* kb = Ks + buf * C::KBUF;
+        const T* vb = Vt + buf * C::VBUF;
         f32x16 sacc[QB][C::NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) sacc[qb][kb] = zero_acc();
+            for (int kb2 = 0; kb2 < C::NKB; ++kb2) sacc[qb][kb2] = zero_acc();
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                const frag af = load_frag<T>(&Ks[(kb * 32 + l32) * C::KS + half * (D / 2) + s * KPL]);
+            for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
+                const frag af = load_frag<T>(&kb[(kb2 * 32 + l32) * C::KS + half * (D / 2) + s * KPL]);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = M::mma(af, qf[qb][s], sacc[qb][kb]);
+                for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = M::mma(af, qf[qb][s], sacc[qb][kb2]);
             }
         }
-
-        // Online softmax, one query column per lane.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int tq = q0 + qb * 32 + l32;
             float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
+            for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float x = sacc[qb][kb][r];
-                    if (diag) {
-                        const int key = j * BN + kb * 32 + acc_row(r, half);
-                        if (key > tq) x = -INFINITY;
+                    if constexpr (MASK) {
+                        const int key = j * BN + kb2 * 32 + acc_row(r, half);
+                        if (key > tq) sacc[qb][kb2][r] = -INFINITY;
                     }
-                    sacc[qb][kb][r] = x;
-                    mx = fmaxf(mx, x);
+                    mx = fmaxf(mx, sacc[qb][kb2][r]);
                 }
             }
-            mx = fmaxf(mx, xor_shfl32(mx));
-            const float mnew = fmaxf(m[qb], mx * a.sl2);
-            const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - msafe);
+            mx = fmaxf(mx, xor_shfl32(mx)) * a.sl2;
+            // Lazy rescale: raise the running max only when this tile exceeds it by > 2^8.
+            const bool grow = mx > mrun[qb] + kRescaleThreshold;
+            if (__builtin_expect(__any(grow), 0)) {
+                const float mnew = grow ? mx : mrun[qb];
+                const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);  // 0 on the first tile
+                l[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                mrun[qb] = mnew;
+            }
+            const float mcur = mrun[qb];
             float rs = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
+            for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[qb][kb][r] * a.sl2 - msafe);
-                    sacc[qb][kb][r] = p;
+                    const float p = __builtin_amdgcn_exp2f(sacc[qb][kb2][r] * a.sl2 - mcur);
+                    sacc[qb][kb2][r] = p;
                     rs += p;
                 }
             }
-            l[qb] = l[qb] * alpha + rs;
-            m[qb] = mnew;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+            l[qb] += rs;
         }
-
-        // O^T += V^T P^T.
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
 #pragma unroll
             for (int ps = 0; ps < C::PS; ++ps) {
                 frag pf[QB];
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) pf[qb] = acc_to_frag<T>(sacc[qb][kb], ps * KPL);
+                for (int qb = 0; qb < QB; ++qb) pf[qb] = acc_to_frag<T>(sacc[qb][kb2], ps * KPL);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const frag vf = load_frag<T>(
-                        &Vt[(db * 32 + l32) * C::VS + kb * 32 + 16 * half + ps * KPL]);
+                    const frag vf = load_frag<T>(&vb[(db * 32 + l32) * C::VS + kb2 * 32 + 16 * half + ps * KPL]);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::mma(vf, pf[qb], oacc[qb][db]);
                 }
             }
         }
+    };
+
+    fetch(0);
+    commit(0);
+    if (jmax >= 1) fetch(1);
+    // The causal diagonal of this wave lies in tile jdiag = q0 / BN (QW divides BN or BN
+    // divides QW); tiles j < q0 / BN need no mask.
+    const int jfirst_masked = q0 / BN;
+    for (int j = 0; j <= jmax; ++j) {
+        __syncthreads();  // tile j visible in buffer j&1; tile j-1's buffer is free
+        if (j + 1 <= jmax) {
+            commit((j + 1) & 1);
+            if (j + 2 <= jmax) fetch(j + 2);
+        }
+        if (!active || j * BN > qlast) continue;
+        if (j >= jfirst_masked)
+            compute(j, j & 1, std::true_type{});
+        else
+            compute(j, j & 1, std::false_type{});
     }
 
     if (!active) return;
@@ -280,7 +335,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                     }
                 }
             }
-            if (half == 0) a.lse[((long long)b * a.Hq + head) * a.T + tq] = (m[qb] + __log2f(lt)) * kLn2;
+            if (half == 0) a.lse[((long long)b * a.Hq + head) * a.T + tq] = (mrun[qb] + __log2f(lt)) * kLn2;
         }
     }
 }
@@ -301,8 +356,10 @@ hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Heads per workgroup: the whole group when it has at most four heads, else the largest
-// divisor of g that is at most four; heads with fewer siblings get more waves each.
+// Heads per workgroup: the largest divisor G of g that is at most four.  Waves per head:
+// two (four when G <= 2) for head_dim <= 64, so a workgroup has 4 to 8 waves of at most
+// ~170 registers; one for head_dim 128 (three or four waves of up to 512 registers).
+template <int D>
 void pick_group(int g, int* G, int* WPH) {
     int G_ = 1;
     for (int c = 4; c >= 1; --c)
@@ -311,18 +368,27 @@ void pick_group(int g, int* G, int* WPH) {
             break;
         }
     *G = G_;
-    *WPH = (G_ == 3) ? 1 : 4 / G_;
+    if (D >= 128)
+        *WPH = (G_ >= 3) ? 1 : 4 / G_;
+    else
+        *WPH = (G_ <= 2) ? 4 : 2;
 }
 
 template <typename T, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     int G, WPH;
-    pick_group(a.Hq / a.Hkv, &G, &WPH);
-    constexpr bool big = (sizeof(T) == 4 && D == 128);
-    constexpr int QB = big ? 1 : 2;
-    constexpr int BN = big ? 32 : 64;
-    if (G * WPH == 3) return launch_fwd_cfg<T, D, QB, BN, 3>(a, G, WPH, stream);
-    return launch_fwd_cfg<T, D, QB, BN, 4>(a, G, WPH, stream);
+    pick_group<D>(a.Hq / a.Hkv, &G, &WPH);
+    constexpr int QB = 1;
+    constexpr int BN = 64;
+    const int nw = G * WPH;
+    if constexpr (D >= 128) {
+        if (nw == 3) return launch_fwd_cfg<T, D, QB, BN, 3>(a, G, WPH, stream);
+        return launch_fwd_cfg<T, D, QB, BN, 4>(a, G, WPH, stream);
+    } else {
+        if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6>(a, G, WPH, stream);
+        if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4>(a, G, WPH, stream);
+        return launch_fwd_cfg<T, D, QB, BN, 8>(a, G, WPH, stream);
+    }
 }
 
 }  // namespace

@@ -17,20 +17,21 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
                            hipStream_t stream);
 
-// Workspace layout of the backward: [dq accumulator fp32 | D_t fp32], 256-byte aligned parts.
+// Workspace of the backward: D_t = sum_d dO * O as fp32 [B, Hq, T], 256-byte aligned.
 size_t bwd_workspace_bytes(int B, int T, int Hq, int D);
 
 // Backward stages (their composition is launch_attn_bwd):
-//   pre:      D_t = sum_d dout * o into the workspace, dq accumulator zeroed;
-//   main:     dk, dv written, dq accumulator filled;
-//   finalize: dq = scale * accumulator in the I/O dtype.
+//   pre:  D_t into the workspace;
+//   dkdv: dk, dv (group-summed) from q, k, v, lse, dout and D_t;
+//   dq:   dq from q, k, v, lse, dout and D_t (independent of dkdv).
 hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
                           int D, IoType dt, hipStream_t stream);
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dk, void* dv, void* workspace, int B, int T,
                            int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream);
-hipError_t launch_bwd_dq_finalize(const void* workspace, void* dq, int B, int T, int Hq, int D,
-                                  float scale, IoType dt, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, void* dq, void* workspace, int B, int T, int Hq,
+                         int Hkv, int D, float scale, IoType dt, hipStream_t stream);
 
 // Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above.
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -82,9 +82,9 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
- * attn_bwd_workspace_size -- bytes of device scratch attn_bwd needs: a float32 dQ
- * accumulator [B, T, Hq, D] and the per-row D_t = sum_d dO * O [B, Hq, T] float32, each
- * rounded up to 256 bytes.  Linear in T (never T^2).  Returns 0 for invalid sizes.
+ * attn_bwd_workspace_size -- bytes of device scratch attn_bwd needs: the per-row
+ * D_t = sum_d dO * O as float32 [B, Hq, T], rounded up to 256 bytes.  Linear in T (never
+ * T^2).  Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt);
 
@@ -93,8 +93,8 @@ size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt
  * forward's q, k, v, o, lse and the upstream gradient dout [B, T, Hq, D].  Outputs, all
  * overwritten (not accumulated):  dq [B, T, Hq, D];  dk, dv [B, T, Hkv, D], each summed
  * over the g query heads that share the K/V head.  The softmax is recomputed tile by tile
- * from lse; D_t = sum_d dout * o.  dq is accumulated in float32 with atomics across key
- * tiles, so its last bits may differ from run to run; o, lse, dk and dv are deterministic.
+ * from lse; D_t = sum_d dout * o.  No atomics are used: dq, dk and dv are bitwise
+ * reproducible from run to run.
  * workspace: device memory of at least attn_bwd_workspace_size(...) bytes, 256-byte
  * aligned, contents on entry ignored, clobbered on return.
  * Errors: as attn_fwd; dq/dk/dv/workspace overlapping any input or each other
@@ -106,27 +106,27 @@ ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    int D, float scale, ea_dtype dt, hipStream_t stream);
 
 /*
- * The three stages of attn_bwd, for callers that schedule them separately (attn_bwd is
- * exactly attn_bwd_preprocess, attn_bwd_main, attn_bwd_dq_finalize on one stream).  They
- * share attn_bwd's workspace, which carries the state from one stage to the next, and take
- * the same sizes; each validates its own pointers and sizes like attn_bwd.
- *  - attn_bwd_preprocess: D_t = sum_d dout * o for every (b, h, t), and the float32 dQ
- *    accumulator set to zero.  Reads o, dout; writes only the workspace.
- *  - attn_bwd_main: the recomputed softmax, dP, dS; writes dk and dv (overwritten,
- *    group-summed) and adds every dQ contribution into the accumulator.  Needs the
- *    preprocess stage's workspace contents.
- *  - attn_bwd_dq_finalize: dq = scale * accumulator, rounded to dt.
+ * The three stages of attn_bwd, for callers that schedule them separately: attn_bwd is
+ * exactly attn_bwd_preprocess, then attn_bwd_dkdv and attn_bwd_dq (in either order, or
+ * concurrently on two streams once the preprocess stage has completed), all with the same
+ * workspace and sizes.  Each validates its own arguments like attn_bwd.
+ *  - attn_bwd_preprocess: D_t = sum_d dout * o for every (b, h, t) into the workspace
+ *    (reads o and dout, writes only the workspace).
+ *  - attn_bwd_dkdv: dk and dv (overwritten, summed over each query-head group); reads the
+ *    workspace written by the preprocess stage.
+ *  - attn_bwd_dq: dq (overwritten); reads the workspace written by the preprocess stage.
  */
 ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
                               size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                               ea_dtype dt, hipStream_t stream);
-ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float* lse,
-                        const void* dout, void* dk, void* dv, void* workspace,
+ea_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dk, void* dv, const void* workspace,
                         size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                         float scale, ea_dtype dt, hipStream_t stream);
-ea_status attn_bwd_dq_finalize(const void* workspace, size_t workspace_bytes, void* dq, int B,
-                               int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
-                               hipStream_t stream);
+ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
+                      int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                      hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* euler_attn_status_string(ea_status s);

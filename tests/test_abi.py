@@ -95,14 +95,14 @@ def test_fwd_validation(L):
 
 
 def test_workspace_size(L):
-    # fp32 dq accumulator + fp32 D_t, each rounded to 256 bytes; linear in T.
+    # fp32 D_t [B, Hq, T] rounded to 256 bytes; linear in T.
     def ws(B, T, Hq, Hkv, D, dt=BF16):
         return L.attn_bwd_workspace_size(B, T, Hq, Hkv, D, dt)
 
     def up(x):
         return (x + 255) // 256 * 256
-    assert ws(4, 1024, 12, 4, 64) == up(4 * 1024 * 12 * 64 * 4) + up(4 * 12 * 1024 * 4)
-    assert ws(1, 3, 1, 1, 32) == up(3 * 32 * 4) + up(3 * 4)
+    assert ws(4, 1024, 12, 4, 64) == up(4 * 12 * 1024 * 4)
+    assert ws(1, 3, 1, 1, 32) == up(3 * 4)
     assert ws(8, 4096, 32, 8, 128) == 2 * ws(8, 2048, 32, 8, 128)
     assert ws(0, 4, 1, 1, 32) == 0
     assert ws(1, 4, 3, 2, 32) == 0
@@ -124,7 +124,7 @@ def test_bwd_validation(L):
     assert bwd(L, D=80) == UNSUP
     assert bwd(L, dk=fake(7) + 2) == ALIGN
     assert bwd(L, ws=fake(9) + 16) == ALIGN          # workspace needs 256-byte alignment
-    assert bwd(L, wsb=1024) == WS
+    assert bwd(L, wsb=L.attn_bwd_workspace_size(2, 16, 4, 2, 64, BF16) - 1) == WS
     assert bwd(L, dq=fake(0)) == ALIAS                # output over an input
     assert bwd(L, dv=fake(7)) == ALIAS                # two outputs
     assert bwd(L, ws=fake(6)) == ALIAS                # workspace over an output
@@ -140,17 +140,19 @@ def test_bwd_stage_validation(L):
     assert pre(w=fake(2) + 64) == ALIGN
     assert pre(wb=ws - 1) == WS
     assert pre(w=fake(1)) == ALIAS
-    main = lambda dk=fake(5), dv=fake(6), w=fake(7), scale=0.1: L.attn_bwd_main(  # noqa
+    dkdv = lambda dk=fake(5), dv=fake(6), w=fake(7), scale=0.1: L.attn_bwd_dkdv(  # noqa
         fake(0), fake(1), fake(2), fake(3), fake(4), dk, dv, w, ws, 2, 16, 4, 2, 64, scale, BF16, None)
-    assert main(dk=None) == NULL
-    assert main(scale=-1.0) == INVALID
-    assert main(dv=fake(5)) == ALIAS
-    assert main(w=fake(4)) == ALIAS
-    fin = lambda w=fake(0), dq=fake(1), wb=ws: L.attn_bwd_dq_finalize(  # noqa
-        w, wb, dq, 2, 16, 4, 2, 64, 0.1, BF16, None)
-    assert fin(dq=None) == NULL
-    assert fin(wb=16) == WS
-    assert fin(dq=fake(0) + 256) == ALIAS
+    assert dkdv(dk=None) == NULL
+    assert dkdv(scale=-1.0) == INVALID
+    assert dkdv(dv=fake(5)) == ALIAS
+    assert dkdv(dk=fake(7)) == ALIAS           # output over the workspace
+    assert dkdv(w=fake(7) + 32) == ALIGN
+    dq = lambda dq=fake(5), w=fake(6), wb=ws: L.attn_bwd_dq(  # noqa
+        fake(0), fake(1), fake(2), fake(3), fake(4), dq, w, wb, 2, 16, 4, 2, 64, 0.1, BF16, None)
+    assert dq(dq=None) == NULL
+    assert dq(wb=16) == WS
+    assert dq(dq=fake(0) + 256) == ALIAS
+    assert dq(dq=fake(6)) == ALIAS
 
 
 def test_binding_refuses_cpu_tensors():
