@@ -12,6 +12,8 @@
 //   2. bwd_dkdv: one workgroup per (64-key tile, K/V head, batch).  K and V stay in
 //      registers; the workgroup walks every head of the group and every query tile on or
 //      below the diagonal, so dK and dV are group-summed in registers and written once.
+//      Q and dO tiles are staged row-major; the Q^T / dO^T operands of dK += dS^T Q and
+//      dV += P^T dO are read with gfx950's transposing LDS read.
 //   3. bwd_dq:   one workgroup per (query tile, K/V head, batch) over the G heads of the
 //      group, shaped like the forward: Q, dO, LSE and D stay in registers, K/V tiles stream
 //      through LDS shared by the group's heads, dQ is written once in the I/O dtype.
@@ -28,27 +30,6 @@ namespace ea {
 namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Two elements of T packed for one LDS store (bf16: one dword; fp32: two dwords).
-template <typename T>
-struct Pair;
-template <>
-struct Pair<bf16> {
-    typedef uint32_t type;
-    __device__ static inline uint32_t make(bf16 a, bf16 b) {
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-    }
-};
-template <>
-struct Pair<float> {
-    typedef float __attribute__((ext_vector_type(2))) type;
-    __device__ static inline type make(float a, float b) { return type{a, b}; }
-};
-
-template <typename T>
-__device__ inline void st_pair(T* p, T a, T b) {
-    *reinterpret_cast<typename Pair<T>::type*>(p) = Pair<T>::make(a, b);
-}
 
 // ---------------------------------------------------------------------------------------
 // 1. D_t = sum_d dO * O per row.
@@ -115,19 +96,17 @@ struct DkdvCfg {
     static constexpr int PS = 16 / KPL;         // MFMA steps over a 32-row accumulator
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;
-    static constexpr int QS = D + EPC;          // row-major Q / dO stride
-    static constexpr int QTS = BM + EPC;        // transposed Q / dO stride
-    static constexpr int NPU = ((BM / 2) * CPR + NT - 1) / NT;  // row-pair units per thread
+    static constexpr int QS = D + EPC;          // row-major Q / dO stride (16 bytes of padding)
+    static constexpr int NCH = (BM * CPR + NT - 1) / NT;  // chunks per thread per tensor
     // LDS carve-up of one stage (bytes); two stages.
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_DO = OFF_Q + sizeof(T) * BM * QS;
-    static constexpr size_t OFF_QT = OFF_DO + sizeof(T) * BM * QS;
-    static constexpr size_t OFF_DOT = OFF_QT + sizeof(T) * D * QTS;
-    static constexpr size_t OFF_LSE = OFF_DOT + sizeof(T) * D * QTS;
+    static constexpr size_t OFF_LSE = OFF_DO + sizeof(T) * BM * QS;
     static constexpr size_t OFF_DT = OFF_LSE + sizeof(float) * BM;
     static constexpr size_t STAGE = (OFF_DT + sizeof(float) * BM + 15) & ~(size_t)15;
     static constexpr size_t BYTES = 2 * STAGE;
-    static constexpr size_t RED_BYTES = (size_t)(NQH - 1) * NKH * 2 * NDB * 16 * 64 * sizeof(float);
+    // One set of dK/dV partials (all key halves) for the final reduction over query blocks.
+    static constexpr size_t RED_BYTES = (size_t)NKH * 2 * NDB * 16 * 64 * sizeof(float);
     static_assert(RED_BYTES <= BYTES, "reduction buffer must fit in the staging region");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -192,28 +171,25 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
     const int nq = a.ntq - i0;
     const int niter = g * nq;
 
-    // Staging of Q_i / dO_i (row pairs), LSE and D: HBM -> registers -> LDS.
-    Vec16<T> qreg[C::NPU][2], dreg[C::NPU][2];
+    // Staging of Q_i / dO_i (16-byte chunks, row-major), LSE and D: HBM -> registers -> LDS.
+    Vec16<T> qreg[C::NCH], dreg[C::NCH];
     float lreg = 0.0f, treg = 0.0f;
     auto fetch = [&](int it) {
         const int head = kvh * g + it / nq;
         const int i = i0 + it % nq;
 #pragma unroll
-        for (int n = 0; n < C::NPU; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BM / 2) * C::CPR) {
-                const int rp = u % (BM / 2), part = u / (BM / 2);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int t = i * BM + 2 * rp + e;
-                    if (t < a.T) {
-                        const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC;
-                        qreg[n][e] = ld16(qp + off);
-                        dreg[n][e] = ld16(dop + off);
-                    } else {
-                        qreg[n][e] = zero16<T>();
-                        dreg[n][e] = zero16<T>();
-                    }
+        for (int n = 0; n < C::NCH; ++n) {
+            const int c = tid + n * C::NT;
+            if (c < BM * C::CPR) {
+                const int row = c / C::CPR, part = c % C::CPR;
+                const int t = i * BM + row;
+                if (t < a.T) {
+                    const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC;
+                    qreg[n] = ld16(qp + off);
+                    dreg[n] = ld16(dop + off);
+                } else {
+                    qreg[n] = zero16<T>();
+                    dreg[n] = zero16<T>();
                 }
             }
         }
@@ -228,26 +204,13 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
         char* base = smem + stage * C::STAGE;
         T* Qs = reinterpret_cast<T*>(base + C::OFF_Q);
         T* dOs = reinterpret_cast<T*>(base + C::OFF_DO);
-        T* QTs = reinterpret_cast<T*>(base + C::OFF_QT);
-        T* dOTs = reinterpret_cast<T*>(base + C::OFF_DOT);
 #pragma unroll
-        for (int n = 0; n < C::NPU; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BM / 2) * C::CPR) {
-                const int rp = u % (BM / 2), part = u / (BM / 2);
-                const int r0 = 2 * rp;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    st16(&Qs[(r0 + e) * C::QS + part * C::EPC], qreg[n][e]);
-                    st16(&dOs[(r0 + e) * C::QS + part * C::EPC], dreg[n][e]);
-                }
-                const int slot = (r0 & ~31) + acc_slot(r0 & 31);  // slot(r0 + 1) == slot + 1
-#pragma unroll
-                for (int e = 0; e < C::EPC; ++e) {
-                    const int d = part * C::EPC + e;
-                    st_pair<T>(&QTs[d * C::QTS + slot], qreg[n][0].get(e), qreg[n][1].get(e));
-                    st_pair<T>(&dOTs[d * C::QTS + slot], dreg[n][0].get(e), dreg[n][1].get(e));
-                }
+        for (int n = 0; n < C::NCH; ++n) {
+            const int c = tid + n * C::NT;
+            if (c < BM * C::CPR) {
+                const int row = c / C::CPR, part = c % C::CPR;
+                st16(&Qs[row * C::QS + part * C::EPC], qreg[n]);
+                st16(&dOs[row * C::QS + part * C::EPC], dreg[n]);
             }
         }
         if (tid < BM) {
@@ -262,8 +225,6 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
         const char* base = smem + stage * C::STAGE;
         const T* Qs = reinterpret_cast<const T*>(base + C::OFF_Q);
         const T* dOs = reinterpret_cast<const T*>(base + C::OFF_DO);
-        const T* QTs = reinterpret_cast<const T*>(base + C::OFF_QT);
-        const T* dOTs = reinterpret_cast<const T*>(base + C::OFF_DOT);
         const float* lse2s = reinterpret_cast<const float*>(base + C::OFF_LSE);
         const float* dts = reinterpret_cast<const float*>(base + C::OFF_DT);
         // S = Q K^T and dP = dO V^T on this wave's 32 x 32 block (lanes = keys).
@@ -298,9 +259,8 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
             const frag dsf = acc_to_frag<T>(dpacc, ps * KPL);
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                const int ro = (db * 32 + l32) * C::QTS + qh * 32 + 16 * half + ps * KPL;
-                dvacc[db] = M::mma(pf, load_frag<T>(&dOTs[ro]), dvacc[db]);
-                dkacc[db] = M::mma(dsf, load_frag<T>(&QTs[ro]), dkacc[db]);
+                dvacc[db] = M::mma(pf, load_rows_frag<T>(dOs, C::QS, qh * 32, ps, db * 32), dvacc[db]);
+                dkacc[db] = M::mma(dsf, load_rows_frag<T>(Qs, C::QS, qh * 32, ps, db * 32), dkacc[db]);
             }
         }
     };
@@ -317,39 +277,40 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
             if (it + 2 < niter) fetch(it + 2);
         }
         const int i = i0 + it % nq;
-        // Mask when the wave's key block reaches past its query block's first row.
-        const bool diag = (j * BN + kh * 32 + 31) > (i * BM + qh * 32);
-        if (diag)
+        // Skip blocks whose keys all follow their queries; mask blocks crossing the diagonal.
+        const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * 32;
+        if (kfirst > qfirst + 31) continue;
+        if (kfirst + 31 > qfirst)
             compute(it, it & 1, std::true_type{});
         else
             compute(it, it & 1, std::false_type{});
     }
 
-    // Reduce the dK/dV partials of the query blocks and store (dK scaled by `scale`).
-    __syncthreads();
+    // Sum the dK/dV partials of the query blocks in LDS, last block first, then store from
+    // the waves of query block 0 (dK scaled by `scale`).  Fixed order: deterministic.
     float* red = reinterpret_cast<float*>(smem);
-    if (qh > 0) {
+    const size_t rbase = (size_t)kh * 2 * C::NDB * 16 * 64;
+    for (int o = C::NQH - 1; o >= 0; --o) {
+        __syncthreads();
+        if (qh == o) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+            for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const size_t base = ((((size_t)(qh - 1) * C::NKH + kh) * 2) * C::NDB + db) * 16 * 64;
-                red[base + r * 64 + lane] = dkacc[db][r];
-                red[base + (size_t)C::NDB * 16 * 64 + r * 64 + lane] = dvacc[db][r];
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const size_t ik = rbase + (size_t)db * 1024 + r * 64 + lane;
+                    const size_t iv = ik + (size_t)C::NDB * 1024;
+                    if (o < C::NQH - 1) {
+                        dkacc[db][r] += red[ik];
+                        dvacc[db][r] += red[iv];
+                    }
+                    if (o > 0) {
+                        red[ik] = dkacc[db][r];
+                        red[iv] = dvacc[db][r];
+                    }
+                }
+        }
     }
-    __syncthreads();
-    if (qh > 0) return;
-    for (int o = 1; o < C::NQH; ++o) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const size_t base = ((((size_t)(o - 1) * C::NKH + kh) * 2) * C::NDB + db) * 16 * 64;
-                dkacc[db][r] += red[base + r * 64 + lane];
-                dvacc[db][r] += red[base + (size_t)C::NDB * 16 * 64 + r * 64 + lane];
-            }
-    }
+    if (qh != 0) return;
     T* __restrict__ dkp = static_cast<T*>(a.dk);
     T* __restrict__ dvp = static_cast<T*>(a.dv);
 #pragma unroll
@@ -378,13 +339,11 @@ struct DqCfg {
     static constexpr int PS = 16 / KPL;
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;
-    static constexpr int KS = D + EPC;   // row-major K / V stride
-    static constexpr int TS = BN + EPC;  // transposed K stride
+    static constexpr int KS = D + EPC;   // row-major K / V stride (16 bytes of padding)
     static constexpr int NT = 64 * NW;
-    static constexpr int NPU = ((BN / 2) * CPR + NT - 1) / NT;  // key-pair units per thread
+    static constexpr int NCH = (BN * CPR + NT - 1) / NT;  // chunks per thread per tensor
     static constexpr int KBUF = BN * KS;
-    static constexpr int TBUF = D * TS;
-    static constexpr int STAGE = 2 * KBUF + TBUF;  // K, V row-major; K^T
+    static constexpr int STAGE = 2 * KBUF;  // K, V row-major
 };
 
 template <typename T, int D, int BN, int NW>
@@ -452,25 +411,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
         }
     }
 
-    // Staging of one K/V tile (pairs of key rows): K and V row-major, K transposed.
-    Vec16<T> kreg[C::NPU][2], vreg[C::NPU][2];
+    // Staging of one K/V tile, row-major 16-byte chunks.
+    Vec16<T> kreg[C::NCH], vreg[C::NCH];
     auto fetch = [&](int j) {
 #pragma unroll
-        for (int n = 0; n < C::NPU; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BN / 2) * C::CPR) {
-                const int kpair = u % (BN / 2), part = u / (BN / 2);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int s = j * BN + 2 * kpair + e;
-                    if (s < a.T) {
-                        const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
-                        kreg[n][e] = ld16(kp + off);
-                        vreg[n][e] = ld16(vp + off);
-                    } else {
-                        kreg[n][e] = zero16<T>();
-                        vreg[n][e] = zero16<T>();
-                    }
+        for (int n = 0; n < C::NCH; ++n) {
+            const int c = tid + n * C::NT;
+            if (c < BN * C::CPR) {
+                const int key = c / C::CPR, part = c % C::CPR;
+                const int s = j * BN + key;
+                if (s < a.T) {
+                    const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
+                    kreg[n] = ld16(kp + off);
+                    vreg[n] = ld16(vp + off);
+                } else {
+                    kreg[n] = zero16<T>();
+                    vreg[n] = zero16<T>();
                 }
             }
         }
@@ -478,22 +434,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     auto commit = [&](int stage) {
         T* Ks = smem + stage * C::STAGE;
         T* Vs = Ks + C::KBUF;
-        T* KT = Vs + C::KBUF;
 #pragma unroll
-        for (int n = 0; n < C::NPU; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BN / 2) * C::CPR) {
-                const int kpair = u % (BN / 2), part = u / (BN / 2);
-                const int k0 = 2 * kpair;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    st16(&Ks[(k0 + e) * C::KS + part * C::EPC], kreg[n][e]);
-                    st16(&Vs[(k0 + e) * C::KS + part * C::EPC], vreg[n][e]);
-                }
-                const int slot = (k0 & ~31) + acc_slot(k0 & 31);
-#pragma unroll
-                for (int e = 0; e < C::EPC; ++e)
-                    st_pair<T>(&KT[(part * C::EPC + e) * C::TS + slot], kreg[n][0].get(e), kreg[n][1].get(e));
+        for (int n = 0; n < C::NCH; ++n) {
+            const int c = tid + n * C::NT;
+            if (c < BN * C::CPR) {
+                const int key = c / C::CPR, part = c % C::CPR;
+                st16(&Ks[key * C::KS + part * C::EPC], kreg[n]);
+                st16(&Vs[key * C::KS + part * C::EPC], vreg[n]);
             }
         }
     };
@@ -506,7 +453,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
         constexpr bool MASK = decltype(masked)::value;
         const T* Ks = smem + stage * C::STAGE;
         const T* Vs = Ks + C::KBUF;
-        const T* KT = Vs + C::KBUF;
         f32x16 sacc[C::NKB], pacc[C::NKB];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
@@ -543,7 +489,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
                 const frag dsf = acc_to_frag<T>(pacc[kb], ps * KPL);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const frag kt = load_frag<T>(&KT[(db * 32 + l32) * C::TS + kb * 32 + 16 * half + ps * KPL]);
+                    const frag kt = load_rows_frag<T>(Ks, C::KS, kb * 32, ps, db * 32);
                     dqacc[db] = M::mma(kt, dsf, dqacc[db]);
                 }
             }
@@ -714,13 +660,14 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
                            const void* dout, void* dk, void* dv, void* workspace, int B, int T,
                            int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
     const BwdArgs a = make_args(q, k, v, lse, dout, nullptr, dk, dv, workspace, B, T, Hq, Hkv, scale);
+    // Query rows per stage: 128 (8 waves) where the registers allow it, else 64 or 32.
     if (dt == kF32) {
-        if (D == 32) return launch_dkdv_t<float, 32, 64>(a, stream);
+        if (D == 32) return launch_dkdv_t<float, 32, 128>(a, stream);
         if (D == 64) return launch_dkdv_t<float, 64, 64>(a, stream);
         return launch_dkdv_t<float, 128, 32>(a, stream);
     }
-    if (D == 32) return launch_dkdv_t<bf16, 32, 64>(a, stream);
-    if (D == 64) return launch_dkdv_t<bf16, 64, 64>(a, stream);
+    if (D == 32) return launch_dkdv_t<bf16, 32, 128>(a, stream);
+    if (D == 64) return launch_dkdv_t<bf16, 64, 128>(a, stream);
     return launch_dkdv_t<bf16, 128, 64>(a, stream);
 }
 

@@ -17,11 +17,12 @@
 //    MFMA tiles: a lane then holds one query column and 16 keys per tile, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two lane halves.
 //    O^T += V^T P^T takes the score registers directly as its B operand.
-//  * K is staged row-major (A operand of S^T); V is staged transposed in "slot" order
-//    (A operand of O^T), written as packed pairs of keys so a wave's LDS stores hit 64
-//    distinct banks.  Rows carry 16 bytes of padding so 16-byte operand reads are
-//    conflict-free.  Two LDS buffers: tile j+1 is committed from registers while tile j is
-//    computed, and tile j+2 is in flight from HBM; one barrier per tile.
+//  * K and V tiles are staged row-major in LDS with 16-byte row padding (16-byte operand
+//    reads conflict-free).  K feeds S^T = K Q^T with plain 16-byte reads; V^T, the A operand
+//    of O^T, is read with gfx950's transposing LDS read (ds_read_b64_tr_b16), so no
+//    transposed copy is ever written.  Two LDS buffers: tile j+1 is committed from
+//    registers while tile j is computed, and tile j+2 is in flight from HBM; one barrier
+//    per tile.
 //  * The online-softmax rescale is lazy: the running max used for exponentiation is raised
 //    only when a row's max grows by more than 2^8 (then O and l are rescaled), so P stays
 //    below 256 and most tiles skip the rescale; the result is exact either way.
@@ -62,30 +63,11 @@ struct FwdCfg {
     static constexpr int PS = 16 / KPL;       // MFMA steps per 32-key block
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;       // 16-byte chunks per K/V row
-    static constexpr int KS = D + EPC;        // K tile row stride (16 bytes of padding)
-    static constexpr int VS = BN + EPC;       // V^T tile row stride
+    static constexpr int KS = D + EPC;        // K / V tile row stride (16 bytes of padding)
     static constexpr int NT = 64 * NW;
-    static constexpr int NCHK = (BN * CPR + NT - 1) / NT;        // K chunks per thread
-    static constexpr int NCHV = ((BN / 2) * CPR + NT - 1) / NT;  // V chunk pairs per thread
+    static constexpr int NCH = (BN * CPR + NT - 1) / NT;  // chunks per thread per tensor
     static constexpr int QW = 32 * QB;
     static constexpr int KBUF = BN * KS;
-    static constexpr int VBUF = D * VS;
-};
-
-// Two elements of T packed for one LDS store (bf16: one dword; fp32: two dwords).
-template <typename T>
-struct Pair;
-template <>
-struct Pair<bf16> {
-    typedef uint32_t type;
-    __device__ static inline uint32_t make(bf16 a, bf16 b) {
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-    }
-};
-template <>
-struct Pair<float> {
-    typedef float __attribute__((ext_vector_type(2))) type;
-    __device__ static inline type make(float a, float b) { return type{a, b}; }
 };
 
 template <typename T, int D, int QB, int BN, int NW>
@@ -96,7 +78,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     constexpr int KPL = C::KPL;
 
     __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
-    __shared__ __attribute__((aligned(16))) T Vt[2 * C::VBUF];
+    __shared__ __attribute__((aligned(16))) T Vs[2 * C::KBUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,57 +129,37 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
     }
 
-    // Staging of one K/V tile: HBM -> registers (fetch) -> LDS (commit).
-    Vec16<T> kreg[C::NCHK], vreg[C::NCHV][2];
+    // Staging of one K/V tile: HBM -> registers (fetch) -> LDS (commit), 16-byte chunks,
+    // consecutive lanes on consecutive chunks of a row.
+    Vec16<T> kreg[C::NCH], vreg[C::NCH];
     auto fetch = [&](int j) {
 #pragma unroll
-        for (int n = 0; n < C::NCHK; ++n) {
+        for (int n = 0; n < C::NCH; ++n) {
             const int c = tid + n * C::NT;
             if (c < BN * C::CPR) {
                 const int key = c / C::CPR, part = c % C::CPR;
                 const int s = j * BN + key;
-                kreg[n] = (s < a.T) ? ld16(kp + ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC)
-                                    : zero16<T>();
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < C::NCHV; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BN / 2) * C::CPR) {
-                const int kpair = u % (BN / 2), part = u / (BN / 2);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int s = j * BN + 2 * kpair + e;
-                    vreg[n][e] = (s < a.T)
-                        ? ld16(vp + ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC)
-                        : zero16<T>();
+                if (s < a.T) {
+                    const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
+                    kreg[n] = ld16(kp + off);
+                    vreg[n] = ld16(vp + off);
+                } else {
+                    kreg[n] = zero16<T>();
+                    vreg[n] = zero16<T>();
                 }
             }
         }
     };
     auto commit = [&](int buf) {
         T* kb = Ks + buf * C::KBUF;
-        T* vb = Vt + buf * C::VBUF;
+        T* vb = Vs + buf * C::KBUF;
 #pragma unroll
-        for (int n = 0; n < C::NCHK; ++n) {
+        for (int n = 0; n < C::NCH; ++n) {
             const int c = tid + n * C::NT;
             if (c < BN * C::CPR) {
                 const int key = c / C::CPR, part = c % C::CPR;
                 st16(&kb[key * C::KS + part * C::EPC], kreg[n]);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < C::NCHV; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < (BN / 2) * C::CPR) {
-                const int kpair = u % (BN / 2), part = u / (BN / 2);
-                const int key = 2 * kpair;
-                const int slot = (key & ~31) + acc_slot(key & 31);  // slot(key + 1) == slot + 1
-#pragma unroll
-                for (int e = 0; e < C::EPC; ++e) {
-                    *reinterpret_cast<typename Pair<T>::type*>(&vb[(part * C::EPC + e) * C::VS + slot]) =
-                        Pair<T>::make(vreg[n][0].get(e), vreg[n][1].get(e));
-                }
+                st16(&vb[key * C::KS + part * C::EPC], vreg[n]);
             }
         }
     };
@@ -216,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     auto compute = [&](int j, int buf, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         const T* kb = Ks + buf * C::KBUF;
-        const T* vb = Vt + buf * C::VBUF;
+        const T* vb = Vs + buf * C::KBUF;
         f32x16 sacc[QB][C::NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -281,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                 for (int qb = 0; qb < QB; ++qb) pf[qb] = acc_to_frag<T>(sacc[qb][kb2], ps * KPL);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const frag vf = load_frag<T>(&vb[(db * 32 + l32) * C::VS + kb2 * 32 + 16 * half + ps * KPL]);
+                    const frag vf = load_rows_frag<T>(vb, C::KS, kb2 * 32, ps, db * 32);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::mma(vf, pf[qb], oacc[qb][db]);
                 }

@@ -14,8 +14,10 @@
 //    run of L/2, so its operand is read with wide loads.
 //  * "accumulator" (over the 32 rows of a C tile reused as an operand): instruction s,
 //    half h, element e  <->  register r = s * KPL + e  <->  row acc_row(r, h).  The partner
-//    operand is stored in LDS in "slot" order slot = 16 * h + r, so a lane again reads one
-//    contiguous run of 16 elements.
+//    operand is read from a row-major LDS tile whose rows are the contraction index with
+//    load_rows_frag: for bf16, two ds_read_b64_tr_b16 transposing reads (each 16-lane group
+//    reads a 4-row x 16-column block and every lane receives one column); for fp32, one
+//    dword per instruction.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -93,6 +95,45 @@ __device__ inline bf16x8 acc_to_frag<bf16>(const f32x16& c, int r0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (bf16)c[r0 + e];  // round to nearest even
     return f;
+}
+
+// Operand fragment for a contraction over 32 "accumulator"-ordered rows of a row-major LDS
+// tile (row = contraction index, column = this lane's MFMA row or column):
+//   lane l, half h = l >> 5, element e of instruction ps  <-  tile[row0 + acc_row(ps*KPL + e, h)]
+//                                                               [col0 + (l & 31)].
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_rows_frag(const T* tile, int stride, int row0,
+                                                        int ps, int col0);
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <>
+__device__ inline bf16x8 load_rows_frag<bf16>(const bf16* tile, int stride, int row0, int ps,
+                                             int col0) {
+    // ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the address of a
+    // 4-element chunk C_j; lane i receives C_{4e + i/4}[i % 4] as element e.  Lane j points
+    // at row (4h + j/4) and columns 16*grp + 4*(j%4) .. +3, so lane i gets column 16*grp + i
+    // of rows 4h + 0..3 (first read) and 8 + 4h + 0..3 (second read): exactly
+    // acc_row(8*ps + e, h) for e = 0..7.
+    const int lane = __lane_id();
+    const int h = lane >> 5, grp = (lane >> 4) & 1, j = lane & 15;
+    const bf16* p = tile + (row0 + 16 * ps + 4 * h + (j >> 2)) * stride + col0 + 16 * grp + 4 * (j & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * stride));
+    bf16x8 f;
+    const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
+    const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    return f;
+}
+
+template <>
+__device__ inline float load_rows_frag<float>(const float* tile, int stride, int row0, int ps,
+                                             int col0) {
+    const int lane = __lane_id();
+    return tile[(row0 + acc_row(ps, lane >> 5)) * stride + col0 + (lane & 31)];
 }
 
 template <typename T>
