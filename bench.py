@@ -2,7 +2,7 @@
 """Benchmark of libeuler_attn: one step = the whole causal-GQA-attention hot path on one
 batch of seeded synthetic inputs already resident in HBM:
 
-    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, dK/dV, dQ) -> RoPE^-1(dQ), RoPE^-1(dK)
+    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, then dQ/dK/dV) -> RoPE^-1(dQ), RoPE^-1(dK)
 
 Throughput is reported as TFLOP/s at the exact causal FLOP count 14 * D * B * Hq * T(T+1)/2
 (4D forward + 10D backward per unmasked query/key pair) and as a fraction of the MI355X
@@ -32,8 +32,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
     "attn_fwd": ["causal_gqa_attention_fwd_amd/csrc/attn_fwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
-    "attn_bwd_dkdv": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
-    "attn_bwd_dq": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_bwd_main": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
 }
 
 
@@ -50,7 +49,7 @@ def sources_sha(paths) -> str:
 
 
 class Step:
-    """Preallocated buffers and the eight launches of one step, called through the C ABI."""
+    """Preallocated buffers and the seven launches of one step, called through the C ABI."""
 
     def __init__(self, w, inp, torch, ea):
         self.w = w
@@ -84,11 +83,9 @@ class Step:
                                       Hkv, D, scale, dtc, stream)),
             ("attn_bwd_pre", L.attn_bwd_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq, Hkv,
                                                      D, dtc, stream)),
-            ("attn_bwd_dkdv", L.attn_bwd_dkdv, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
-                                                p(self.dk), p(self.dv), p(self.ws), nws, B, T, Hq, Hkv, D,
-                                                scale, dtc, stream)),
-            ("attn_bwd_dq", L.attn_bwd_dq, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
-                                            p(self.dq), p(self.ws), nws, B, T, Hq, Hkv, D, scale, dtc, stream)),
+            ("attn_bwd_main", L.attn_bwd_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
+                                                p(self.dq), p(self.dk), p(self.dv), p(self.ws), nws, B, T,
+                                                Hq, Hkv, D, scale, dtc, stream)),
             ("rope_inv_dq", L.rope_apply, (p(self.dq), p(self.dq_raw), B, T, Hq, D, dtc, base, 0, 1, stream)),
             ("rope_inv_dk", L.rope_apply, (p(self.dk), p(self.dk_raw), B, T, Hkv, D, dtc, base, 0, 1, stream)),
         ]
@@ -118,12 +115,10 @@ def algorithmic(w) -> dict:
         "rope_q": {"bytes": 2 * qb}, "rope_k": {"bytes": 2 * kb},
         "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
         "attn_bwd_pre": {"bytes": 2 * qb + lse},
-        # The backward's 10D per pair: S recompute, dP, dV, dK (8D) in the dK/dV kernel, the dQ
-        # product (2D) in the dQ kernel, which also recomputes S and dP (4D executed, not
-        # counted as algorithmic work).
-        "attn_bwd_dkdv": {"flops": 8 * w.D * w.pairs, "bytes": 2 * qb + 2 * kb + 2 * lse + 2 * kb},
-        "attn_bwd_dq": {"flops": 2 * w.D * w.pairs, "executed_flops": 6 * w.D * w.pairs,
-                        "bytes": 2 * qb + 2 * kb + 2 * lse + qb},
+        # The backward's 10D per pair (S recompute, dP, dV, dK, dQ); the dQ-role workgroups
+        # recompute S and dP once more (4D per pair executed, not counted as algorithmic).
+        "attn_bwd_main": {"flops": 10 * w.D * w.pairs, "executed_flops": 14 * w.D * w.pairs,
+                          "bytes": 2 * qb + 2 * kb + 2 * lse + qb + 2 * kb},
         "rope_inv_dq": {"bytes": 2 * qb}, "rope_inv_dk": {"bytes": 2 * kb},
     }
 
@@ -235,6 +230,9 @@ def main() -> int:
     ap.add_argument("--extra", default="long_t8192",
                     help="comma-separated extra workloads timed the same way (reported under 'extra')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (known bytes) five times, for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -249,6 +247,15 @@ def main() -> int:
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 2
     ea.lib()  # fail loudly when the HIP library is missing
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 5}))
+        return 0
 
     w, step, ms, wall, kern_us = time_workload(args.workload, args.steps, args.warmup, torch, ea, W)
     tflops = w.flops_total() / (ms * 1e-3) / 1e12
@@ -268,7 +275,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), causal=True,
-                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_dkdv,attn_bwd_dq,"
+                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_main,"
                             "rope_inv_dq,rope_inv_dk"),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": w.flops_total(),
@@ -277,8 +284,7 @@ def main() -> int:
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline_for(w, kern_us, dominant),
         "roofline_attn_fwd": roofline_for(w, kern_us, "attn_fwd"),
-        "roofline_attn_bwd_dkdv": roofline_for(w, kern_us, "attn_bwd_dkdv"),
-        "roofline_attn_bwd_dq": roofline_for(w, kern_us, "attn_bwd_dq"),
+        "roofline_attn_bwd_main": roofline_for(w, kern_us, "attn_bwd_main"),
     }
     extra = {}
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:

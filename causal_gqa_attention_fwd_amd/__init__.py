@@ -22,7 +22,7 @@ import os
 import torch
 
 __all__ = ["rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
-           "attn_bwd_dkdv", "attn_bwd_dq", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.restype = ci
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, vp]
     L.attn_bwd_preprocess.restype = ci
+    L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_main.restype = ci
     L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_bwd_dkdv.restype = ci
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -201,6 +203,19 @@ def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, workspace: torch.Te
         st = lib().attn_bwd_preprocess(o.data_ptr(), dout.data_ptr(), wp, wb, B, T, Hq, Hkv, D,
                                        _dtype_code(o), _stream(o.device))
     _raise(st, "attn_bwd_preprocess")
+
+
+def attn_bwd_main(q, k, v, lse, dout, workspace, dq, dk, dv, scale: float | None = None) -> None:
+    """Backward stage 2 in one launch: dq, dk, dv; needs the preprocess workspace."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    wp, wb = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb,
+                                 B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd_main")
 
 
 def attn_bwd_dkdv(q, k, v, lse, dout, workspace, dk, dv, scale: float | None = None) -> None:

@@ -196,6 +196,26 @@ ea_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float
                                         B, T, Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
 }
 
+ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                        size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                        float scale, ea_dtype dt, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {q, k, v, static_cast<const void*>(lse), dout, static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(lse, z.lseb),
+                         range(dout, z.qb), range(workspace, z.ws)};
+    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, const_cast<void*>(workspace),
+                                        B, T, Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
+}
+
 ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                       const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
                       int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,

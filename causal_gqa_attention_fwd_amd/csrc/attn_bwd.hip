@@ -7,14 +7,16 @@
 //   dV_s = sum_{h in group} sum_{t>=s} P_ts dO_t
 //   dK_s = scale * sum_{h in group} sum_{t>=s} dS_ts Q_t
 //   dQ_t = scale * sum_{s<=t} dS_ts K_s
-// Three launches, none of them with atomics, so every output is deterministic:
+// Two launches, no atomics, so every output is deterministic:
 //   1. bwd_pre:  D_t for every (b, h, t), into the workspace.
-//   2. bwd_dkdv: one workgroup per (64-key tile, K/V head, batch).  K and V stay in
+//   then bwd_kernel, whose workgroups take one of two roles (one launch per role, or one
+//   launch with both roles interleaved when the problem is small):
+//   2. dK/dV role: one workgroup per (64-key tile, K/V head, batch).  K and V stay in
 //      registers; the workgroup walks every head of the group and every query tile on or
 //      below the diagonal, so dK and dV are group-summed in registers and written once.
 //      Q and dO tiles are staged row-major; the Q^T / dO^T operands of dK += dS^T Q and
 //      dV += P^T dO are read with gfx950's transposing LDS read.
-//   3. bwd_dq:   one workgroup per (query tile, K/V head, batch) over the G heads of the
+//   3. dQ role:   one workgroup per (query tile, K/V head, batch) over the G heads of the
 //      group, shaped like the forward: Q, dO, LSE and D stay in registers, K/V tiles stream
 //      through LDS shared by the group's heads, dQ is written once in the I/O dtype.
 // Splitting dQ out costs the S and dP products a second time (14D instead of 10D FLOPs per
@@ -73,9 +75,11 @@ struct BwdArgs {
     void* dk;
     void* dv;
     int B, T, Hq, Hkv;
-    int G, WPH, nhc;  // dq kernel: heads per workgroup, waves per head, head chunks
-    int ntk;          // key tiles
-    int ntq;          // query tiles
+    int G, WPH, nhc;  // dq role: heads per workgroup, waves per head, head chunks
+    int ntk;          // dK/dV role: 64-key tiles
+    int ntq;          // dK/dV role: query stages (BM rows each)
+    int ntq_dq;       // dq role: query tiles (32 * WPH rows each)
+    int roles;        // 1: dK/dV only, 2: dQ only, 3: both in one launch
     float sl2;        // scale * log2(e)
     float scale;
 };
@@ -111,15 +115,14 @@ struct DkdvCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+// One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.
 template <typename T, int D, int BM>
-__global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, int kvh, int b) {
     using C = DkdvCfg<T, D, BM>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
     constexpr int BN = C::BN;
-
-    __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -128,12 +131,6 @@ __global__ __launch_bounds__((64 * DkdvCfg<T, D, BM>::NW)) void bwd_dkdv_kernel(
     const int l32 = lane & 31;
     const int kh = w % C::NKH;
     const int qh = w / C::NKH;
-
-    const int HB = a.B * a.Hkv;
-    const int j = blockIdx.x / HB;
-    const int rem = blockIdx.x % HB;
-    const int kvh = rem % a.Hkv;
-    const int b = rem / a.Hkv;
     const int g = a.Hq / a.Hkv;
 
     const T* __restrict__ qp = static_cast<const T*>(a.q);
@@ -346,14 +343,16 @@ struct DqCfg {
     static constexpr int STAGE = 2 * KBUF;  // K, V row-major
 };
 
+// One workgroup of the dQ role: item it (0 = the longest query tile) of K/V head kvh in
+// batch b.  Waves beyond G * WPH stay in the staging loop but never compute.
 template <typename T, int D, int BN, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it, int kvh, int b) {
     using C = DqCfg<T, D, BN, NW>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
 
-    __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+    T* smem = reinterpret_cast<T*>(smem_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -361,20 +360,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
-    const int HB = a.B * a.Hkv * a.nhc;
-    const int L = blockIdx.x;
-    const int tile = a.ntq - 1 - L / HB;
-    const int rem = L % HB;
-    const int hc = rem % a.nhc;
-    const int kvh = (rem / a.nhc) % a.Hkv;
-    const int b = rem / (a.nhc * a.Hkv);
+    const int tile = a.ntq_dq - 1 - it / a.nhc;
+    const int hc = it % a.nhc;
     const int g = a.Hq / a.Hkv;
     const int BM = a.WPH * 32;
-    const int hs = w / a.WPH;
-    const int sub = w % a.WPH;
+    const bool wave_used = w < a.G * a.WPH;
+    const int hs = wave_used ? w / a.WPH : 0;
+    const int sub = wave_used ? w % a.WPH : 0;
     const int head = kvh * g + hc * a.G + hs;
     const int q0 = tile * BM + sub * 32;
-    const bool active = q0 < a.T;
+    const bool active = wave_used && q0 < a.T;
     const int wg_last = min(tile * BM + BM, a.T) - 1;
     const int jmax = wg_last / BN;
     const int tq = q0 + l32;  // this lane's query
@@ -538,8 +533,68 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Launchers.
+// One launch for both roles.  Items are numbered per (batch, K/V head): dK/dV items
+// j = 0 .. ntk-1 (key tile j, heaviest first) and dQ items i = 0 .. nqi-1 (heaviest first).
+// With both roles, the two lists are merged by relative position (j/ntk vs i/nqi), so the
+// heavy items of both roles are dispatched first and each role's light tail overlaps the
+// other's work.
 // ---------------------------------------------------------------------------------------
+struct Sched {
+    int ntk, nqi;
+};
+
+__device__ inline int dkdv_rank(int j, const Sched& s) {  // merged position of dK/dV item j
+    return j + (int)(((long long)j * s.nqi + s.ntk - 1) / s.ntk);
+}
+
+template <typename T, int D, int NW>
+struct BwdKernelCfg {
+    static constexpr int BM = 16 * NW;  // dK/dV role: 2 key halves x NW/2 query blocks
+    static constexpr int BNQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // dQ role key tile
+    using Dk = DkdvCfg<T, D, BM>;
+    using Dq = DqCfg<T, D, BNQ, NW>;
+    static constexpr size_t DQ_BYTES = 2 * (size_t)Dq::STAGE * sizeof(T);
+    static constexpr size_t BYTES = Dk::BYTES > DQ_BYTES ? Dk::BYTES : DQ_BYTES;
+    static_assert(Dk::NW == NW, "dK/dV role must use every wave");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
+    using K = BwdKernelCfg<T, D, NW>;
+    __shared__ __attribute__((aligned(16))) char smem[K::BYTES];
+    const int HB = a.B * a.Hkv;
+    const int m = blockIdx.x / HB;
+    const int rem = blockIdx.x % HB;
+    const int kvh = rem % a.Hkv;
+    const int b = rem / a.Hkv;
+    const int nqi = a.ntq_dq * a.nhc;
+    bool is_dkdv;
+    int item;
+    if (a.roles == 1) {
+        is_dkdv = true;
+        item = m;
+    } else if (a.roles == 2) {
+        is_dkdv = false;
+        item = m;
+    } else {
+        // Largest j with dkdv_rank(j) <= m (dkdv_rank is increasing, dkdv_rank(0) = 0).
+        const Sched sc{a.ntk, nqi};
+        int lo = 0, hi = a.ntk - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (dkdv_rank(mid, sc) <= m) lo = mid;
+            else hi = mid - 1;
+        }
+        is_dkdv = dkdv_rank(lo, sc) == m;
+        item = is_dkdv ? lo : m - (lo + 1);
+    }
+    if (is_dkdv)
+        dkdv_role<T, D, K::BM>(a, smem, item, kvh, b);
+    else
+        dq_role<T, D, K::BNQ, NW>(a, smem, item, kvh, b);
+}
+
 template <typename T, int D>
 hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, int seq, int Hq,
                         hipStream_t stream) {
@@ -553,22 +608,11 @@ hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, in
     return hipGetLastError();
 }
 
-template <typename T, int D, int BM>
-hipError_t launch_dkdv_t(const BwdArgs& a0, hipStream_t stream) {
-    BwdArgs a = a0;
-    using C = DkdvCfg<T, D, BM>;
-    a.ntk = (a.T + C::BN - 1) / C::BN;
-    a.ntq = (a.T + BM - 1) / BM;
-    const long long blocks = (long long)a.ntk * a.B * a.Hkv;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BM>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
-    return hipGetLastError();
-}
-
-// Same grouping rule as the forward: G = largest divisor of g that is at most four; two
-// waves per head (four when G <= 2) for head_dim <= 64, one for head_dim 128.
+// Heads per dQ workgroup: the largest divisor G of g that is at most four, with two waves
+// per head (four when G <= 2) for head_dim <= 64, i.e. 4, 6 or 8 waves; for head_dim 128
+// one wave per head (G >= 3) or 4/G, in a 4-wave workgroup.
 template <int D>
-void pick_dq_group(int g, int* G, int* WPH) {
+void pick_dq_shape(int g, int* G, int* WPH) {
     int G_ = 1;
     for (int c = 4; c >= 1; --c)
         if (g % c == 0) {
@@ -582,34 +626,68 @@ void pick_dq_group(int g, int* G, int* WPH) {
         *WPH = (G_ <= 2) ? 4 : 2;
 }
 
+// Waves of a dK/dV workgroup (2 key halves x NW/2 query blocks of 32 rows).
+template <typename T, int D>
+constexpr int dkdv_waves() {
+    return (D >= 128 || (sizeof(T) == 4 && D == 64)) ? 4 : 8;
+}
+
 template <typename T, int D, int NW>
-hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) {
+hipError_t launch_bwd_cfg(const BwdArgs& a0, int G, int WPH, int roles, hipStream_t stream) {
+    using K = BwdKernelCfg<T, D, NW>;
     BwdArgs a = a0;
-    constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // LDS budget of fp32 / D=128
     a.G = G;
     a.WPH = WPH;
     a.nhc = (a.Hq / a.Hkv) / G;
-    const int BM = WPH * 32;
-    a.ntq = (a.T + BM - 1) / BM;
-    const long long blocks = (long long)a.ntq * a.B * a.Hkv * a.nhc;
+    a.ntk = (a.T + K::Dk::BN - 1) / K::Dk::BN;
+    a.ntq = (a.T + K::BM - 1) / K::BM;
+    a.ntq_dq = (a.T + WPH * 32 - 1) / (WPH * 32);
+    a.roles = roles;
+    long long items = 0;
+    if (roles & 1) items += a.ntk;
+    if (roles & 2) items += (long long)a.ntq_dq * a.nhc;
+    const long long blocks = items * a.B * a.Hkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
-    int G, WPH;
-    pick_dq_group<D>(a.Hq / a.Hkv, &G, &WPH);
+hipError_t launch_dq_only(const BwdArgs& a, int G, int WPH, hipStream_t stream) {
     const int nw = G * WPH;
     if constexpr (D >= 128) {
-        if (nw == 3) return launch_dq_cfg<T, D, 3>(a, G, WPH, stream);
-        return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
+        return launch_bwd_cfg<T, D, 4>(a, G, WPH, 2, stream);
     } else {
-        if (nw == 6) return launch_dq_cfg<T, D, 6>(a, G, WPH, stream);
-        if (nw == 4) return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
-        return launch_dq_cfg<T, D, 8>(a, G, WPH, stream);
+        if (nw == 6) return launch_bwd_cfg<T, D, 6>(a, G, WPH, 2, stream);
+        if (nw == 4) return launch_bwd_cfg<T, D, 4>(a, G, WPH, 2, stream);
+        return launch_bwd_cfg<T, D, 8>(a, G, WPH, 2, stream);
     }
+}
+
+// roles: 1 = dK/dV, 2 = dQ, 3 = both.  Both roles share one launch when the dK/dV role alone
+// would not fill the chip twice over (then each role's causal tail overlaps the other's
+// work); otherwise they run as two launches, each with its own workgroup shape.
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
+    constexpr int NWK = dkdv_waves<T, D>();
+    int G, WPH;
+    pick_dq_shape<D>(a.Hq / a.Hkv, &G, &WPH);
+    const long long dkdv_blocks = (long long)((a.T + 63) / 64) * a.B * a.Hkv;
+    const bool fuse = roles == 3 && G * WPH <= NWK && dkdv_blocks <= 256;
+    if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
+    if (roles & 1) {
+        hipError_t e = launch_bwd_cfg<T, D, NWK>(a, G, WPH, 1, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (roles & 2) return launch_dq_only<T, D>(a, G, WPH, stream);
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_bwd_roles(const BwdArgs& a, int D, int roles, hipStream_t stream) {
+    if (D == 32) return launch_bwd_t<T, 32>(a, roles, stream);
+    if (D == 64) return launch_bwd_t<T, 64>(a, roles, stream);
+    return launch_bwd_t<T, 128>(a, roles, stream);
 }
 
 float* ws_dt(void* ws) { return static_cast<float*>(ws); }
@@ -660,29 +738,22 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
                            const void* dout, void* dk, void* dv, void* workspace, int B, int T,
                            int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
     const BwdArgs a = make_args(q, k, v, lse, dout, nullptr, dk, dv, workspace, B, T, Hq, Hkv, scale);
-    // Query rows per stage: 128 (8 waves) where the registers allow it, else 64 or 32.
-    if (dt == kF32) {
-        if (D == 32) return launch_dkdv_t<float, 32, 128>(a, stream);
-        if (D == 64) return launch_dkdv_t<float, 64, 64>(a, stream);
-        return launch_dkdv_t<float, 128, 32>(a, stream);
-    }
-    if (D == 32) return launch_dkdv_t<bf16, 32, 128>(a, stream);
-    if (D == 64) return launch_dkdv_t<bf16, 64, 128>(a, stream);
-    return launch_dkdv_t<bf16, 128, 64>(a, stream);
+    return dt == kF32 ? launch_bwd_roles<float>(a, D, 1, stream) : launch_bwd_roles<bf16>(a, D, 1, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                          const void* dout, void* dq, void* workspace, int B, int T, int Hq,
                          int Hkv, int D, float scale, IoType dt, hipStream_t stream) {
     const BwdArgs a = make_args(q, k, v, lse, dout, dq, nullptr, nullptr, workspace, B, T, Hq, Hkv, scale);
-    if (dt == kF32) {
-        if (D == 32) return launch_dq_t<float, 32>(a, stream);
-        if (D == 64) return launch_dq_t<float, 64>(a, stream);
-        return launch_dq_t<float, 128>(a, stream);
-    }
-    if (D == 32) return launch_dq_t<bf16, 32>(a, stream);
-    if (D == 64) return launch_dq_t<bf16, 64>(a, stream);
-    return launch_dq_t<bf16, 128>(a, stream);
+    return dt == kF32 ? launch_bwd_roles<float>(a, D, 2, stream) : launch_bwd_roles<bf16>(a, D, 2, stream);
+}
+
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
+                           int T, int Hq, int Hkv, int D, float scale, IoType dt,
+                           hipStream_t stream) {
+    const BwdArgs a = make_args(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, scale);
+    return dt == kF32 ? launch_bwd_roles<float>(a, D, 3, stream) : launch_bwd_roles<bf16>(a, D, 3, stream);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -691,9 +762,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            IoType dt, hipStream_t stream) {
     hipError_t e = launch_bwd_pre(o, dout, workspace, B, T, Hq, D, dt, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dkdv(q, k, v, lse, dout, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
-    if (e != hipSuccess) return e;
-    return launch_bwd_dq(q, k, v, lse, dout, dq, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
+    return launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
 }
 
 }  // namespace ea

@@ -32,6 +32,11 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                          const void* dout, void* dq, void* workspace, int B, int T, int Hq,
                          int Hkv, int D, float scale, IoType dt, hipStream_t stream);
+// dkdv and dq in one launch (the two roles' workgroups interleaved, heaviest first).
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
+                           int T, int Hq, int Hkv, int D, float scale, IoType dt,
+                           hipStream_t stream);
 
 // Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above.
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -106,19 +106,25 @@ ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    int D, float scale, ea_dtype dt, hipStream_t stream);
 
 /*
- * The three stages of attn_bwd, for callers that schedule them separately: attn_bwd is
- * exactly attn_bwd_preprocess, then attn_bwd_dkdv and attn_bwd_dq (in either order, or
- * concurrently on two streams once the preprocess stage has completed), all with the same
- * workspace and sizes.  Each validates its own arguments like attn_bwd.
+ * The stages of attn_bwd, for callers that schedule them separately: attn_bwd is exactly
+ * attn_bwd_preprocess followed by attn_bwd_main; attn_bwd_main computes what attn_bwd_dkdv
+ * and attn_bwd_dq compute (in either order, or concurrently on two streams, once the
+ * preprocess stage has completed) in a single launch.  All share attn_bwd's workspace and
+ * sizes, and each validates its own arguments like attn_bwd.
  *  - attn_bwd_preprocess: D_t = sum_d dout * o for every (b, h, t) into the workspace
  *    (reads o and dout, writes only the workspace).
- *  - attn_bwd_dkdv: dk and dv (overwritten, summed over each query-head group); reads the
- *    workspace written by the preprocess stage.
- *  - attn_bwd_dq: dq (overwritten); reads the workspace written by the preprocess stage.
+ *  - attn_bwd_main: dq, dk and dv (overwritten; dk, dv summed over each query-head group).
+ *  - attn_bwd_dkdv: dk and dv only.
+ *  - attn_bwd_dq: dq only.
+ * The last three read the workspace written by the preprocess stage.
  */
 ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
                               size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                               ea_dtype dt, hipStream_t stream);
+ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                        size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                        float scale, ea_dtype dt, hipStream_t stream);
 ea_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                         const void* dout, void* dk, void* dv, const void* workspace,
                         size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,

@@ -147,6 +147,12 @@ def test_bwd_stage_validation(L):
     assert dkdv(dv=fake(5)) == ALIAS
     assert dkdv(dk=fake(7)) == ALIAS           # output over the workspace
     assert dkdv(w=fake(7) + 32) == ALIGN
+    mn = lambda dq=fake(5), dk=fake(6), dv=fake(7), w=fake(8): L.attn_bwd_main(  # noqa
+        fake(0), fake(1), fake(2), fake(3), fake(4), dq, dk, dv, w, ws, 2, 16, 4, 2, 64, 0.1, BF16, None)
+    assert mn(dv=None) == NULL
+    assert mn(dq=fake(6)) == ALIAS
+    assert mn(dk=fake(2)) == ALIAS
+    assert mn(w=fake(8) + 16) == ALIGN
     dq = lambda dq=fake(5), w=fake(6), wb=ws: L.attn_bwd_dq(  # noqa
         fake(0), fake(1), fake(2), fake(3), fake(4), dq, w, wb, 2, 16, 4, 2, 64, 0.1, BF16, None)
     assert dq(dq=None) == NULL

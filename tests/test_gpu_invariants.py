@@ -152,3 +152,7 @@ def test_backward_stages_compose(dt):
     ea.attn_bwd_dkdv(q, k, v, lse, do, ws, dk2, dv2)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    dq3, dk3, dv3 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ea.attn_bwd_main(q, k, v, lse, do, ws, dq3, dk3, dv3)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
