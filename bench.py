@@ -49,7 +49,7 @@ def sources_sha(paths) -> str:
 
 
 class Step:
-    """Preallocated buffers and the seven launches of one step, called through the C ABI."""
+    """Preallocated buffers and the five launches of one step, called through the C ABI."""
 
     def __init__(self, w, inp, torch, ea):
         self.w = w
@@ -77,8 +77,8 @@ class Step:
         p = lambda t: t.data_ptr()  # noqa: E731
         # (name, ctypes function, arguments) for each launch, in order.
         self.calls = [
-            ("rope_q", L.rope_apply, (p(self.q_raw), p(self.qr), B, T, Hq, D, dtc, base, 0, 0, stream)),
-            ("rope_k", L.rope_apply, (p(self.k_raw), p(self.kr), B, T, Hkv, D, dtc, base, 0, 0, stream)),
+            ("rope_qk", L.rope_apply_qk, (p(self.q_raw), p(self.qr), Hq, p(self.k_raw), p(self.kr), Hkv, B, T,
+                                          D, dtc, base, 0, 0, stream)),
             ("attn_fwd", L.attn_fwd, (p(self.qr), p(self.kr), p(self.v), p(self.o), p(self.lse), B, T, Hq,
                                       Hkv, D, scale, dtc, stream)),
             ("attn_bwd_pre", L.attn_bwd_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq, Hkv,
@@ -86,8 +86,8 @@ class Step:
             ("attn_bwd_main", L.attn_bwd_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
                                                 p(self.dq), p(self.dk), p(self.dv), p(self.ws), nws, B, T,
                                                 Hq, Hkv, D, scale, dtc, stream)),
-            ("rope_inv_dq", L.rope_apply, (p(self.dq), p(self.dq_raw), B, T, Hq, D, dtc, base, 0, 1, stream)),
-            ("rope_inv_dk", L.rope_apply, (p(self.dk), p(self.dk_raw), B, T, Hkv, D, dtc, base, 0, 1, stream)),
+            ("rope_inv_dqdk", L.rope_apply_qk, (p(self.dq), p(self.dq_raw), Hq, p(self.dk), p(self.dk_raw), Hkv,
+                                                B, T, D, dtc, base, 0, 1, stream)),
         ]
 
     def run(self):
@@ -112,14 +112,14 @@ def algorithmic(w) -> dict:
     kb = w.B * w.T * w.Hkv * w.D * es
     lse = w.B * w.Hq * w.T * 4
     return {
-        "rope_q": {"bytes": 2 * qb}, "rope_k": {"bytes": 2 * kb},
+        "rope_qk": {"bytes": 2 * qb + 2 * kb},
         "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
         "attn_bwd_pre": {"bytes": 2 * qb + lse},
         # The backward's 10D per pair (S recompute, dP, dV, dK, dQ); the dQ-role workgroups
         # recompute S and dP once more (4D per pair executed, not counted as algorithmic).
         "attn_bwd_main": {"flops": 10 * w.D * w.pairs, "executed_flops": 14 * w.D * w.pairs,
                           "bytes": 2 * qb + 2 * kb + 2 * lse + qb + 2 * kb},
-        "rope_inv_dq": {"bytes": 2 * qb}, "rope_inv_dk": {"bytes": 2 * kb},
+        "rope_inv_dqdk": {"bytes": 2 * qb + 2 * kb},
     }
 
 
@@ -275,8 +275,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), causal=True,
-                       step="rope_q,rope_k,attn_fwd,attn_bwd_pre,attn_bwd_main,"
-                            "rope_inv_dq,rope_inv_dk"),
+                       step="rope_qk,attn_fwd,attn_bwd_pre,attn_bwd_main,rope_inv_dqdk"),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": w.flops_total(),
         "flops_convention": "exact causal: 14*D*B*Hq*T(T+1)/2",

@@ -21,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
+__all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     vp, ci, cd, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
     L.rope_apply.argtypes = [vp, vp, ci, ci, ci, ci, ci, cd, ci, ci, vp]
     L.rope_apply.restype = ci
+    L.rope_apply_qk.argtypes = [vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, cd, ci, ci, vp]
+    L.rope_apply_qk.restype = ci
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_fwd.restype = ci
     L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -114,6 +116,29 @@ def rope_apply(x: torch.Tensor, base: float = 10000.0, pos0: int = 0, inverse: b
                               int(pos0), int(bool(inverse)), _stream(x.device))
     _raise(st, "rope_apply")
     return y
+
+
+def rope_apply_qk(q: torch.Tensor, k: torch.Tensor, base: float = 10000.0, pos0: int = 0,
+                  inverse: bool = False, q_out: torch.Tensor | None = None,
+                  k_out: torch.Tensor | None = None):
+    """rope_apply on q [B,T,Hq,D] and k [B,T,Hkv,D] in one launch; returns (q_out, k_out)."""
+    _check("q", q, 4)
+    _check("k", k, 4, q.device, q.dtype)
+    if k.shape[0] != q.shape[0] or k.shape[1] != q.shape[1] or k.shape[3] != q.shape[3]:
+        raise ValueError("q and k must share B, T and D")
+    qo = torch.empty_like(q) if q_out is None else q_out
+    ko = torch.empty_like(k) if k_out is None else k_out
+    _check("q_out", qo, 4, q.device, q.dtype)
+    _check("k_out", ko, 4, q.device, q.dtype)
+    if qo.shape != q.shape or ko.shape != k.shape:
+        raise ValueError("outputs must match their inputs' shapes")
+    B, T, Hq, D = q.shape
+    with torch.cuda.device(q.device):
+        st = lib().rope_apply_qk(q.data_ptr(), qo.data_ptr(), Hq, k.data_ptr(), ko.data_ptr(), k.shape[2],
+                                 B, T, D, _dtype_code(q), float(base), int(pos0), int(bool(inverse)),
+                                 _stream(q.device))
+    _raise(st, "rope_apply_qk")
+    return qo, ko
 
 
 def _shapes(q, k, v):

@@ -78,6 +78,25 @@ ea_status rope_apply(const void* x, void* y, int B, int T, int H, int D, ea_dtyp
                                     inverse, stream));
 }
 
+ea_status rope_apply_qk(const void* q, void* q_out, int Hq, const void* k, void* k_out, int Hkv,
+                        int B, int T, int D, ea_dtype dt, double base, int pos0, int inverse,
+                        hipStream_t stream) {
+    if (!q || !q_out || !k || !k_out) return EA_ERR_NULL;
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 2 || (D % 2) != 0 || pos0 < 0) return EA_ERR_INVALID_ARG;
+    if (!std::isfinite(base) || !(base > 1.0) || (inverse != 0 && inverse != 1)) return EA_ERR_INVALID_ARG;
+    if (!dtype_ok(dt) || D > 256 || (D % 8) != 0) return EA_ERR_UNSUPPORTED;
+    if ((long long)pos0 + T > (1LL << 31)) return EA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(q_out) || !aligned16(k) || !aligned16(k_out)) return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const Range rq = range(q, (size_t)B * T * Hq * D * es), rqo = range(q_out, (size_t)B * T * Hq * D * es);
+    const Range rk = range(k, (size_t)B * T * Hkv * D * es), rko = range(k_out, (size_t)B * T * Hkv * D * es);
+    // Each output may equal its own input exactly; no other overlap.
+    if ((q != q_out && overlap(rq, rqo)) || (k != k_out && overlap(rk, rko))) return EA_ERR_ALIAS;
+    if (overlap(rqo, rk) || overlap(rqo, rko) || overlap(rko, rq) || overlap(rq, rk)) return EA_ERR_ALIAS;
+    return from_hip(ea::launch_rope_pair(q, q_out, Hq, k, k_out, Hkv, B, T, D,
+                                         static_cast<ea::IoType>(dt), base, pos0, inverse, stream));
+}
+
 ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return EA_ERR_NULL;

@@ -12,6 +12,11 @@ enum IoType { kF32 = 0, kBF16 = 1 };
 hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoType dt,
                        double base, int pos0, int inverse, hipStream_t stream);
 
+// RoPE of two tensors sharing (B, T, D) in one launch: x0 [B,T,H0,D] -> y0, x1 [B,T,H1,D] -> y1.
+hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1,
+                            int B, int T, int D, IoType dt, double base, int pos0, int inverse,
+                            hipStream_t stream);
+
 // Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log).
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,

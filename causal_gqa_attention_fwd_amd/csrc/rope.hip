@@ -5,7 +5,8 @@
 // kernel implements the adjacent-pair reading: pair (2i, 2i+1) of row (b, t, h) turns by
 // phi = (pos0 + t) * theta_i, theta_i = base^(-2i/D), and by -phi for the inverse.
 //
-// Work is HBM-bound (one read and one write of x).  Each thread owns one 16-byte chunk of
+// Work is HBM-bound (one read and one write of x).  Two tensors that share (B, T, D) --
+// Q and K, or dQ and dK -- can be rotated in one launch.  Each thread owns one 16-byte chunk of
 // a row (8 bf16 or 4 fp32 elements) for HPT heads of the same position: the angles of its
 // pairs are formed once, in float64 (product and reduction modulo 2*pi), and reused for
 // every head.  sin/cos of the reduced angle, |r| <= pi, are float32.  Consecutive lanes
@@ -27,14 +28,28 @@ constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
 constexpr double kInvTwoPi = 0.15915494309189535;
 constexpr int kHeadsPerThread = 4;
 
+// Up to two tensors [B, T, H_k, D] in one launch (Q and K, or dQ and dK): units
+// [0, n0) belong to tensor 0, [n0, n0 + n1) to tensor 1.
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(const T* x, T* y, long long nunits, int seq,
-                                                   int H, int D, int pos0, int inverse,
-                                                   RopeFreq f) {
+struct RopeJob {
+    const T* x[2];
+    T* y[2];
+    int H[2];
+    long long n0, ntot;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int D, int pos0,
+                                                   int inverse, RopeFreq f) {
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int PPC = EPC / 2;         // pairs per chunk
-    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (u >= nunits) return;
+    long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= job.ntot) return;
+    const int which = u < job.n0 ? 0 : 1;
+    if (which) u -= job.n0;
+    const T* x = job.x[which];
+    T* y = job.y[which];
+    const int H = job.H[which];
     const int cpr = D / EPC;  // chunks per row
     const int nhb = (H + kHeadsPerThread - 1) / kHeadsPerThread;
     const int c = (int)(u % cpr);
@@ -73,20 +88,29 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* x, T* y, long long n
 }
 
 template <typename T>
-hipError_t launch_rope_t(const void* x, void* y, int B, int seq, int H, int D, double base,
-                         int pos0, int inverse, hipStream_t stream) {
+hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1, int B,
+                         int seq, int D, double base, int pos0, int inverse, hipStream_t stream) {
     constexpr int EPC = 16 / sizeof(T);
     RopeFreq f;
     for (int i = 0; i < D / 2; ++i) f.theta[i] = std::pow(base, -2.0 * (double)i / (double)D);
     for (int i = D / 2; i < 128; ++i) f.theta[i] = 0.0;
-    const int nhb = (H + kHeadsPerThread - 1) / kHeadsPerThread;
-    const long long nunits = (long long)B * seq * nhb * (D / EPC);
+    RopeJob<T> job;
+    job.x[0] = static_cast<const T*>(x0);
+    job.y[0] = static_cast<T*>(y0);
+    job.H[0] = H0;
+    job.x[1] = static_cast<const T*>(x1);
+    job.y[1] = static_cast<T*>(y1);
+    job.H[1] = H1;
+    auto units = [&](int H) {
+        return H > 0 ? (long long)B * seq * ((H + kHeadsPerThread - 1) / kHeadsPerThread) * (D / EPC) : 0LL;
+    };
+    job.n0 = units(H0);
+    job.ntot = job.n0 + units(H1);
     const int threads = 256;
-    const long long blocks = (nunits + threads - 1) / threads;
+    const long long blocks = (job.ntot + threads - 1) / threads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(rope_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       static_cast<const T*>(x), static_cast<T*>(y), nunits, seq, H, D, pos0,
-                       inverse, f);
+    hipLaunchKernelGGL(rope_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, stream, job, seq, D,
+                       pos0, inverse, f);
     return hipGetLastError();
 }
 
@@ -94,8 +118,15 @@ hipError_t launch_rope_t(const void* x, void* y, int B, int seq, int H, int D, d
 
 hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoType dt,
                        double base, int pos0, int inverse, hipStream_t stream) {
-    if (dt == kF32) return launch_rope_t<float>(x, y, B, T, H, D, base, pos0, inverse, stream);
-    return launch_rope_t<bf16>(x, y, B, T, H, D, base, pos0, inverse, stream);
+    if (dt == kF32) return launch_rope_t<float>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, inverse, stream);
+    return launch_rope_t<bf16>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, inverse, stream);
+}
+
+hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1,
+                            int B, int T, int D, IoType dt, double base, int pos0, int inverse,
+                            hipStream_t stream) {
+    if (dt == kF32) return launch_rope_t<float>(x0, y0, H0, x1, y1, H1, B, T, D, base, pos0, inverse, stream);
+    return launch_rope_t<bf16>(x0, y0, H0, x1, y1, H1, B, T, D, base, pos0, inverse, stream);
 }
 
 }  // namespace ea

@@ -69,6 +69,16 @@ ea_status rope_apply(const void* x, void* y, int B, int T, int H, int D, ea_dtyp
                      double base, int pos0, int inverse, hipStream_t stream);
 
 /*
+ * rope_apply_qk -- rope_apply on two tensors that share (B, T, D) in one launch: q [B,T,Hq,D]
+ * into q_out and k [B,T,Hkv,D] into k_out (the queries and keys before attn_fwd, or with
+ * inverse = 1 the gradients dQ and dK after attn_bwd).  Same arithmetic, layouts and errors
+ * as rope_apply; each output may equal its own input exactly, no other overlap is allowed.
+ */
+ea_status rope_apply_qk(const void* q, void* q_out, int Hq, const void* k, void* k_out, int Hkv,
+                        int B, int T, int D, ea_dtype dt, double base, int pos0, int inverse,
+                        hipStream_t stream);
+
+/*
  * attn_fwd -- causal GQA attention forward.  For every batch b, query head h and query
  * position t:  S_ts = scale * <q_t, k_s> for s <= t;  O_t = sum_s softmax_s(S_t.) v_s;
  * LSE_t = log sum_{s<=t} exp(S_ts).  q and k are expected to carry RoPE already.

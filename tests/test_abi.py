@@ -73,6 +73,19 @@ def test_rope_validation(L):
     # y == x is allowed: it passes validation (and would launch), so not called here.
 
 
+def test_rope_qk_validation(L):
+    def r(q=fake(0), qo=fake(1), Hq=4, k=fake(2), ko=fake(3), Hkv=2, D=64, inv=0):
+        return L.rope_apply_qk(q, qo, Hq, k, ko, Hkv, 2, 16, D, BF16, 1e4, 0, inv, None)
+    assert r(k=None) == NULL
+    assert r(Hkv=0) == INVALID
+    assert r(inv=3) == INVALID
+    assert r(D=12) == UNSUP
+    assert r(ko=fake(3) + 8) == ALIGN
+    assert r(ko=fake(2) + 64) == ALIAS          # k_out partially over k
+    assert r(qo=fake(2)) == ALIAS               # q_out over k
+    assert r(k=fake(0) + 1024) == ALIAS         # k inside q
+
+
 def fwd(L, q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), B=2, T=16, Hq=4, Hkv=2,
         D=64, scale=0.125, dt=BF16):
     return L.attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, None)

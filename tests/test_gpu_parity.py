@@ -151,3 +151,25 @@ def test_rope_variants(dt, D, H, T, base, pos0):
     ea.rope_apply(z, base, pos0, out=z)
     torch.cuda.synchronize()
     assert torch.equal(z, y)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rope_qk_one_launch(dt):
+    # The two-tensor launch equals two single-tensor launches bitwise, and the oracle.
+    say("[parity] rope_apply_qk dt=%s" % dt)
+    q = W.make_random((2, 77, 12, 64), 501, dt).cuda()
+    k = W.make_random((2, 77, 4, 64), 502, dt).cuda()
+    for inverse in (False, True):
+        qo, ko = ea.rope_apply_qk(q, k, 10000.0, pos0=3, inverse=inverse)
+        q1 = ea.rope_apply(q, 10000.0, pos0=3, inverse=inverse)
+        k1 = ea.rope_apply(k, 10000.0, pos0=3, inverse=inverse)
+        torch.cuda.synchronize()
+        assert torch.equal(qo, q1) and torch.equal(ko, k1)
+        check_rope(dt, qo, q, 10000.0, "q", pos0=3, inverse=inverse)
+        check_rope(dt, ko, k, 10000.0, "k", pos0=3, inverse=inverse)
+    # in place on both
+    q2, k2 = q.clone(), k.clone()
+    ea.rope_apply_qk(q2, k2, 10000.0, q_out=q2, k_out=k2)
+    qo, ko = ea.rope_apply_qk(q, k, 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, qo) and torch.equal(k2, ko)
