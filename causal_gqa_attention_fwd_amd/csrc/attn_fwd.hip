@@ -26,6 +26,10 @@
 //  * The online-softmax rescale is lazy: the running max used for exponentiation is raised
 //    only when a row's max grows by more than 2^8 (then O and l are rescaled), so P stays
 //    below 256 and most tiles skip the rescale; the result is exact either way.
+//  * Small problems (too few query blocks to fill the chip twice) split each query block's
+//    key range over KSPL = 2 waves that take alternate K/V tiles; their (max, sum, output)
+//    partials merge exactly through LDS at the end.  This halves the serial work of the
+//    longest (last) query blocks, which set the kernel's duration under causal masking.
 //  * Tiles strictly above the diagonal are never visited; the causal mask is evaluated only
 //    on the one tile that crosses a wave's diagonal.  The launch order puts the longest
 //    (latest) query tiles first; workgroups of one K/V head land on the same XCD.
@@ -54,7 +58,7 @@ struct FwdArgs {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest un-normalised P
 
-template <typename T, int D, int QB, int BN, int NW>
+template <typename T, int D, int QB, int BN, int NW, int KSPL>
 struct FwdCfg {
     static constexpr int KPL = Mfma<T>::KPL;
     static constexpr int NS = D / (2 * KPL);  // MFMA steps over head_dim
@@ -63,22 +67,26 @@ struct FwdCfg {
     static constexpr int PS = 16 / KPL;       // MFMA steps per 32-key block
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;       // 16-byte chunks per K/V row
-    static constexpr int KS = D + EPC;        // K / V tile row stride (16 bytes of padding)
+    static constexpr int KSTR = D + EPC;      // K / V tile row stride (16 bytes of padding)
     static constexpr int NT = 64 * NW;
-    static constexpr int NCH = (BN * CPR + NT - 1) / NT;  // chunks per thread per tensor
+    static constexpr int NCH = (KSPL * BN * CPR + NT - 1) / NT;  // chunks per thread per tensor
     static constexpr int QW = 32 * QB;
-    static constexpr int KBUF = BN * KS;
+    static constexpr int KBUF = BN * KSTR;
+    static constexpr int NBUF = 2 * KSPL;     // double buffer per key split
+    // Merge area for the key splits' partials (reuses the K tiles after the loop).
+    static constexpr int MERGE_FLOATS = (NW / KSPL) * (16 * (D / 32) * QB + 2 * QB) * 64;
+    static_assert(KSPL == 1 || MERGE_FLOATS * 4 <= (int)(NBUF * KBUF * sizeof(T)), "merge area");
 };
 
-template <typename T, int D, int QB, int BN, int NW>
+template <typename T, int D, int QB, int BN, int NW, int KSPL>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
-    using C = FwdCfg<T, D, QB, BN, NW>;
+    using C = FwdCfg<T, D, QB, BN, NW, KSPL>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
 
-    __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
-    __shared__ __attribute__((aligned(16))) T Vs[2 * C::KBUF];
+    __shared__ __attribute__((aligned(16))) T Ks[C::NBUF * C::KBUF];
+    __shared__ __attribute__((aligned(16))) T Vs[C::NBUF * C::KBUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,8 +103,11 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     const int b = rem / (a.nhc * a.Hkv);
     const int g = a.Hq / a.Hkv;
     const int BM = a.WPH * C::QW;
-    const int hs = w / a.WPH;
-    const int sub = w % a.WPH;
+    const int nws = a.G * a.WPH;      // waves per key split
+    const int ks = w / nws;           // this wave's key split: tiles j with j % KSPL == ks
+    const int slot = w % nws;
+    const int hs = slot / a.WPH;
+    const int sub = slot % a.WPH;
     const int head = kvh * g + hc * a.G + hs;
     const int q0 = tile * BM + sub * C::QW;
     const bool active = q0 < a.T;
@@ -129,17 +140,19 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
     }
 
-    // Staging of one K/V tile: HBM -> registers (fetch) -> LDS (commit), 16-byte chunks,
-    // consecutive lanes on consecutive chunks of a row.
+    // Staging of one step (KSPL consecutive K/V tiles): HBM -> registers (fetch) -> LDS
+    // (commit), 16-byte chunks, consecutive lanes on consecutive chunks of a row.
     Vec16<T> kreg[C::NCH], vreg[C::NCH];
-    auto fetch = [&](int j) {
+    auto fetch = [&](int step) {
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
-            const int c = tid + n * C::NT;
-            if (c < BN * C::CPR) {
+            const int u = tid + n * C::NT;
+            if (u < KSPL * BN * C::CPR) {
+                const int sp = u / (BN * C::CPR), c = u % (BN * C::CPR);
                 const int key = c / C::CPR, part = c % C::CPR;
+                const int j = step * KSPL + sp;
                 const int s = j * BN + key;
-                if (s < a.T) {
+                if (j <= jmax && s < a.T) {
                     const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
                     kreg[n] = ld16(kp + off);
                     vreg[n] = ld16(vp + off);
@@ -151,15 +164,15 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
     };
     auto commit = [&](int buf) {
-        T* kb = Ks + buf * C::KBUF;
-        T* vb = Vs + buf * C::KBUF;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
-            const int c = tid + n * C::NT;
-            if (c < BN * C::CPR) {
+            const int u = tid + n * C::NT;
+            if (u < KSPL * BN * C::CPR) {
+                const int sp = u / (BN * C::CPR), c = u % (BN * C::CPR);
                 const int key = c / C::CPR, part = c % C::CPR;
-                st16(&kb[key * C::KS + part * C::EPC], kreg[n]);
-                st16(&vb[key * C::KS + part * C::EPC], vreg[n]);
+                const int o = (sp * 2 + buf) * C::KBUF + key * C::KSTR + part * C::EPC;
+                st16(&Ks[o], kreg[n]);
+                st16(&Vs[o], vreg[n]);
             }
         }
     };
@@ -177,8 +190,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
     auto compute = [&](int j, int buf, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
-        const T* kb = Ks + buf * C::KBUF;
-        const T* vb = Vs + buf * C::KBUF;
+        const T* kb = Ks + (ks * 2 + buf) * C::KBUF;
+        const T* vb = Vs + (ks * 2 + buf) * C::KBUF;
         f32x16 sacc[QB][C::NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
             for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
-                const frag af = load_frag<T>(&kb[(kb2 * 32 + l32) * C::KS + half * (D / 2) + s * KPL]);
+                const frag af = load_frag<T>(&kb[(kb2 * 32 + l32) * C::KSTR + half * (D / 2) + s * KPL]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = M::mma(af, qf[qb][s], sacc[qb][kb2]);
             }
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                 for (int qb = 0; qb < QB; ++qb) pf[qb] = acc_to_frag<T>(sacc[qb][kb2], ps * KPL);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const frag vf = load_rows_frag<T>(vb, C::KS, kb2 * 32, ps, db * 32);
+                    const frag vf = load_rows_frag<T>(vb, C::KSTR, kb2 * 32, ps, db * 32);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::mma(vf, pf[qb], oacc[qb][db]);
                 }
@@ -251,23 +264,62 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
     };
 
+    const int nsteps = jmax / KSPL + 1;
     fetch(0);
     commit(0);
-    if (jmax >= 1) fetch(1);
-    // The causal diagonal of this wave lies in tile jdiag = q0 / BN (QW divides BN or BN
-    // divides QW); tiles j < q0 / BN need no mask.
+    if (nsteps > 1) fetch(1);
+    // The causal diagonal of this wave lies in tile q0 / BN; earlier tiles need no mask.
     const int jfirst_masked = q0 / BN;
-    for (int j = 0; j <= jmax; ++j) {
-        __syncthreads();  // tile j visible in buffer j&1; tile j-1's buffer is free
-        if (j + 1 <= jmax) {
-            commit((j + 1) & 1);
-            if (j + 2 <= jmax) fetch(j + 2);
+    for (int st = 0; st < nsteps; ++st) {
+        __syncthreads();  // step st visible in buffer st&1; step st-1's buffer is free
+        if (st + 1 < nsteps) {
+            commit((st + 1) & 1);
+            if (st + 2 < nsteps) fetch(st + 2);
         }
-        if (!active || j * BN > qlast) continue;
+        const int j = st * KSPL + ks;
+        if (!active || j > jmax || j * BN > qlast) continue;
         if (j >= jfirst_masked)
-            compute(j, j & 1, std::true_type{});
+            compute(j, st & 1, std::true_type{});
         else
-            compute(j, j & 1, std::false_type{});
+            compute(j, st & 1, std::false_type{});
+    }
+
+    if constexpr (KSPL == 2) {
+        // Merge the two key splits: m = max(m0, m1), a_i = 2^(m_i - m),
+        // l = a0 l0 + a1 l1, O = a0 O0 + a1 O1 (per lane, before the halves combine).
+        constexpr int PER = 16 * C::NDB * QB + 2 * QB;
+        float* mb = reinterpret_cast<float*>(Ks) + (size_t)slot * PER * 64;
+        __syncthreads();  // every wave is done with the K/V tiles
+        if (ks == 1 && active) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mb[((qb * C::NDB + db) * 16 + r) * 64 + lane] = oacc[qb][db][r];
+                mb[(16 * C::NDB * QB + 2 * qb) * 64 + lane] = mrun[qb];
+                mb[(16 * C::NDB * QB + 2 * qb + 1) * 64 + lane] = l[qb];
+            }
+        }
+        __syncthreads();
+        if (ks == 1) return;
+        if (active) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m1 = mb[(16 * C::NDB * QB + 2 * qb) * 64 + lane];
+                const float l1 = mb[(16 * C::NDB * QB + 2 * qb + 1) * 64 + lane];
+                const float m = fmaxf(mrun[qb], m1);  // finite: split 0 always has tile 0
+                const float a0 = __builtin_amdgcn_exp2f(mrun[qb] - m);
+                const float a1 = __builtin_amdgcn_exp2f(m1 - m);  // 0 when split 1 saw no tile
+                l[qb] = l[qb] * a0 + l1 * a1;
+                mrun[qb] = m;
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        oacc[qb][db][r] = oacc[qb][db][r] * a0 + mb[((qb * C::NDB + db) * 16 + r) * 64 + lane] * a1;
+            }
+        }
     }
 
     if (!active) return;
@@ -302,7 +354,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     }
 }
 
-template <typename T, int D, int QB, int BN, int NW>
+template <typename T, int D, int QB, int BN, int NW, int KSPL>
 hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream) {
     FwdArgs a = a0;
     const int g = a.Hq / a.Hkv;
@@ -313,16 +365,20 @@ hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream)
     a.ntq = (a.T + BM - 1) / BM;
     const long long blocks = (long long)a.ntq * a.B * a.Hkv * a.nhc;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BN, NW>), dim3((unsigned)blocks), dim3(64 * NW),
-                       0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BN, NW, KSPL>), dim3((unsigned)blocks),
+                       dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
-// Heads per workgroup: the largest divisor G of g that is at most four.  Waves per head:
-// two (four when G <= 2) for head_dim <= 64, so a workgroup has 4 to 8 waves of at most
-// ~170 registers; one for head_dim 128 (three or four waves of up to 512 registers).
-template <int D>
-void pick_group(int g, int* G, int* WPH) {
+// Heads per workgroup: the largest divisor G of g that is at most four.
+// * head_dim <= 64, bf16, few query blocks (B * Hq * T / 32 <= 2048, i.e. fewer than two
+//   waves per SIMD): one 32-row block per head (two for G <= 2) and two key splits.
+// * head_dim <= 64 otherwise: two waves per head (four when G <= 2), no key split.
+// * head_dim 128: one wave per head (4/G when G <= 2), no key split (LDS and registers).
+// Every shape gives 4, 6 or 8 waves (3 or 4 for head_dim 128).
+template <typename T, int D>
+void pick_fwd_shape(const FwdArgs& a, int* G, int* WPH, int* KSPL) {
+    const int g = a.Hq / a.Hkv;
     int G_ = 1;
     for (int c = 4; c >= 1; --c)
         if (g % c == 0) {
@@ -330,26 +386,40 @@ void pick_group(int g, int* G, int* WPH) {
             break;
         }
     *G = G_;
-    if (D >= 128)
+    const long long qblocks = (long long)a.B * a.Hq * ((a.T + 31) / 32);
+    if (D >= 128) {
         *WPH = (G_ >= 3) ? 1 : 4 / G_;
-    else
+        *KSPL = 1;
+    } else if (sizeof(T) == 2 && qblocks <= 2048) {
+        *WPH = (G_ <= 2) ? 2 : 1;
+        *KSPL = 2;
+    } else {
         *WPH = (G_ <= 2) ? 4 : 2;
+        *KSPL = 1;
+    }
 }
 
 template <typename T, int D>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-    int G, WPH;
-    pick_group<D>(a.Hq / a.Hkv, &G, &WPH);
+    int G, WPH, KSPL;
+    pick_fwd_shape<T, D>(a, &G, &WPH, &KSPL);
     constexpr int QB = 1;
     constexpr int BN = 64;
-    const int nw = G * WPH;
+    const int nw = G * WPH * KSPL;
     if constexpr (D >= 128) {
-        if (nw == 3) return launch_fwd_cfg<T, D, QB, BN, 3>(a, G, WPH, stream);
-        return launch_fwd_cfg<T, D, QB, BN, 4>(a, G, WPH, stream);
+        if (nw == 3) return launch_fwd_cfg<T, D, QB, BN, 3, 1>(a, G, WPH, stream);
+        return launch_fwd_cfg<T, D, QB, BN, 4, 1>(a, G, WPH, stream);
     } else {
-        if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6>(a, G, WPH, stream);
-        if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4>(a, G, WPH, stream);
-        return launch_fwd_cfg<T, D, QB, BN, 8>(a, G, WPH, stream);
+        if constexpr (sizeof(T) == 2) {
+            if (KSPL == 2) {
+                if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6, 2>(a, G, WPH, stream);
+                if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4, 2>(a, G, WPH, stream);
+                return launch_fwd_cfg<T, D, QB, BN, 8, 2>(a, G, WPH, stream);
+            }
+        }
+        if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6, 1>(a, G, WPH, stream);
+        if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4, 1>(a, G, WPH, stream);
+        return launch_fwd_cfg<T, D, QB, BN, 8, 1>(a, G, WPH, stream);
     }
 }
 
