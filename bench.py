@@ -2,7 +2,8 @@
 """Benchmark of libeuler_attn: one step = the whole causal-GQA-attention hot path on one
 batch of seeded synthetic inputs already resident in HBM:
 
-    RoPE(Q), RoPE(K) -> attn_fwd -> attn_bwd (pre-pass, then dQ/dK/dV) -> RoPE^-1(dQ), RoPE^-1(dK)
+    RoPE(Q), RoPE(K) (one launch) -> attn_fwd -> attn_bwd_rope: pre-pass (D_t and the RoPE
+    table), then dQ/dK/dV with RoPE^-1 applied to dQ and dK as they are stored
 
 Throughput is reported as TFLOP/s at the exact causal FLOP count 14 * D * B * Hq * T(T+1)/2
 (4D forward + 10D backward per unmasked query/key pair) and as a fraction of the MI355X
@@ -62,32 +63,29 @@ class Step:
         self.kr = torch.empty_like(self.k_raw)
         self.o = torch.empty_like(self.q_raw)
         self.lse = torch.empty((w.B, w.Hq, w.T), device=dev, dtype=torch.float32)
-        self.dq = torch.empty_like(self.q_raw)
-        self.dk = torch.empty_like(self.k_raw)
-        self.dv = torch.empty_like(self.v)
         self.dq_raw = torch.empty_like(self.q_raw)
         self.dk_raw = torch.empty_like(self.k_raw)
+        self.dv = torch.empty_like(self.v)
         dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
-        nws = ea.attn_bwd_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, self.q_raw.dtype)
+        nws = ea.attn_bwd_rope_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, self.q_raw.dtype)
         self.ws = torch.empty(nws, device=dev, dtype=torch.uint8)
         L = ea.lib()
         scale = 1.0 / (w.D ** 0.5)
         stream = torch.cuda.current_stream(dev).cuda_stream
         B, T, Hq, Hkv, D, base = w.B, w.T, w.Hq, w.Hkv, w.D, w.base
         p = lambda t: t.data_ptr()  # noqa: E731
-        # (name, ctypes function, arguments) for each launch, in order.
+        # (name, ctypes function, arguments) for each launch, in order.  The backward returns the
+        # gradients of the raw (pre-RoPE) Q and K: the RoPE backward is fused into its stores.
         self.calls = [
             ("rope_qk", L.rope_apply_qk, (p(self.q_raw), p(self.qr), Hq, p(self.k_raw), p(self.kr), Hkv, B, T,
                                           D, dtc, base, 0, 0, stream)),
             ("attn_fwd", L.attn_fwd, (p(self.qr), p(self.kr), p(self.v), p(self.o), p(self.lse), B, T, Hq,
                                       Hkv, D, scale, dtc, stream)),
-            ("attn_bwd_pre", L.attn_bwd_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq, Hkv,
-                                                     D, dtc, stream)),
-            ("attn_bwd_main", L.attn_bwd_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse), p(self.do),
-                                                p(self.dq), p(self.dk), p(self.dv), p(self.ws), nws, B, T,
-                                                Hq, Hkv, D, scale, dtc, stream)),
-            ("rope_inv_dqdk", L.rope_apply_qk, (p(self.dq), p(self.dq_raw), Hq, p(self.dk), p(self.dk_raw), Hkv,
-                                                B, T, D, dtc, base, 0, 1, stream)),
+            ("attn_bwd_pre", L.attn_bwd_rope_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq,
+                                                          Hkv, D, dtc, base, 0, stream)),
+            ("attn_bwd_main", L.attn_bwd_rope_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse),
+                                                     p(self.do), p(self.dq_raw), p(self.dk_raw), p(self.dv),
+                                                     p(self.ws), nws, B, T, Hq, Hkv, D, scale, dtc, stream)),
         ]
 
     def run(self):
@@ -114,12 +112,13 @@ def algorithmic(w) -> dict:
     return {
         "rope_qk": {"bytes": 2 * qb + 2 * kb},
         "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
-        "attn_bwd_pre": {"bytes": 2 * qb + lse},
+        # D_t (read O and dO, write D_t) and the RoPE (cos, sin) table, fp32 [T, D/2, 2].
+        "attn_bwd_pre": {"bytes": 2 * qb + lse + w.T * w.D * 4},
         # The backward's 10D per pair (S recompute, dP, dV, dK, dQ); the dQ-role workgroups
         # recompute S and dP once more (4D per pair executed, not counted as algorithmic).
+        # The inverse RoPE on dQ and dK is applied before their stores (no extra HBM pass).
         "attn_bwd_main": {"flops": 10 * w.D * w.pairs, "executed_flops": 14 * w.D * w.pairs,
                           "bytes": 2 * qb + 2 * kb + 2 * lse + qb + 2 * kb},
-        "rope_inv_dqdk": {"bytes": 2 * qb + 2 * kb},
     }
 
 
@@ -275,7 +274,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), causal=True,
-                       step="rope_qk,attn_fwd,attn_bwd_pre,attn_bwd_main,rope_inv_dqdk"),
+                       step="rope_qk,attn_fwd,attn_bwd_rope_preprocess,attn_bwd_rope_main"),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": w.flops_total(),
         "flops_convention": "exact causal: 14*D*B*Hq*T(T+1)/2",

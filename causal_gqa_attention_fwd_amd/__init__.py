@@ -9,6 +9,8 @@ built, or the tensors are not on a ROCm device, the calls raise.
     rope_apply(x, base=1e4, pos0=0, inverse=False, out=None) -> y
     attn_fwd(q, k, v, scale=None, out=None, lse=None)        -> (o, lse)
     attn_bwd(q, k, v, o, lse, dout, scale=None, ...)         -> (dq, dk, dv)
+    attn_bwd_rope(q, k, v, o, lse, dout, base=1e4, pos0=0, ...)
+                         -> (dq, dk, dv) with dq, dk for the tensors before RoPE
 
 Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
 dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
@@ -22,7 +24,8 @@ import os
 import torch
 
 __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
-           "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
+           "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
@@ -60,6 +63,14 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dkdv.restype = ci
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_bwd_dq.restype = ci
+    L.attn_bwd_rope_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_bwd_rope_workspace_size.restype = sz
+    L.attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, cd, ci, vp]
+    L.attn_bwd_rope.restype = ci
+    L.attn_bwd_rope_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cd, ci, vp]
+    L.attn_bwd_rope_preprocess.restype = ci
+    L.attn_bwd_rope_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_rope_main.restype = ci
     L.euler_attn_status_string.argtypes = [ci]
     L.euler_attn_status_string.restype = ctypes.c_char_p
     L.euler_attn_version.argtypes = []
@@ -177,11 +188,30 @@ def attn_bwd_workspace_size(B: int, T: int, Hq: int, Hkv: int, D: int, dtype=tor
     return int(lib().attn_bwd_workspace_size(B, T, Hq, Hkv, D, code))
 
 
+def attn_bwd_rope_workspace_size(B: int, T: int, Hq: int, Hkv: int, D: int, dtype=torch.bfloat16) -> int:
+    code = EA_F32 if dtype == torch.float32 else EA_BF16
+    return int(lib().attn_bwd_rope_workspace_size(B, T, Hq, Hkv, D, code))
+
+
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
              workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
              dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
     """Causal GQA attention backward; returns (dq, dk, dv), dk/dv summed over each group."""
+    return _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, None)
+
+
+def attn_bwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                  lse: torch.Tensor, dout: torch.Tensor, base: float = 10000.0, pos0: int = 0,
+                  scale: float | None = None, workspace: torch.Tensor | None = None,
+                  dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                  dv: torch.Tensor | None = None):
+    """attn_bwd with the RoPE backward fused in: q, k are the rotated tensors attn_fwd saw;
+    dq, dk are returned for the tensors before rope_apply(base, pos0).  Returns (dq, dk, dv)."""
+    return _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, (float(base), int(pos0)))
+
+
+def _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, rope):
     B, T, Hq, Hkv, D = _shapes(q, k, v)
     _check("o", o, 4, q.device, q.dtype)
     _check("dout", dout, 4, q.device, q.dtype)
@@ -197,18 +227,22 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         _check(name, t, 4, q.device, q.dtype)
         if t.shape != ref.shape:
             raise ValueError("%s has the wrong shape" % name)
-    need = int(lib().attn_bwd_workspace_size(B, T, Hq, Hkv, D, _dtype_code(q)))
+    wsfn = lib().attn_bwd_workspace_size if rope is None else lib().attn_bwd_rope_workspace_size
+    need = int(wsfn(B, T, Hq, Hkv, D, _dtype_code(q)))
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the device of q")
     nbytes = workspace.numel() * workspace.element_size()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes, B, T, Hq, Hkv, D,
+            float(scale), _dtype_code(q))
     with torch.cuda.device(q.device):
-        st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                            workspace.data_ptr(), nbytes, B, T, Hq, Hkv, D, float(scale),
-                            _dtype_code(q), _stream(q.device))
-    _raise(st, "attn_bwd")
+        if rope is None:
+            st = lib().attn_bwd(*args, _stream(q.device))
+        else:
+            st = lib().attn_bwd_rope(*args, rope[0], rope[1], _stream(q.device))
+    _raise(st, "attn_bwd" if rope is None else "attn_bwd_rope")
     return dq, dk, dv
 
 
@@ -219,7 +253,7 @@ def _ws_args(workspace: torch.Tensor, device) -> tuple:
 
 
 def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, workspace: torch.Tensor, Hkv: int) -> None:
-    """Backward stage 1: D_t = sum_d dout * o into the workspace; zero the dQ accumulator."""
+    """Backward stage 1: D_t = sum_d dout * o into the workspace."""
     _check("o", o, 4)
     _check("dout", dout, 4, o.device, o.dtype)
     B, T, Hq, D = o.shape
@@ -267,3 +301,29 @@ def attn_bwd_dq(q, k, v, lse, dout, workspace, dq, scale: float | None = None) -
                                dout.data_ptr(), dq.data_ptr(), wp, wb, B, T, Hq, Hkv, D,
                                float(scale), _dtype_code(q), _stream(q.device))
     _raise(st, "attn_bwd_dq")
+
+
+def attn_bwd_rope_preprocess(o: torch.Tensor, dout: torch.Tensor, workspace: torch.Tensor, Hkv: int,
+                             base: float = 10000.0, pos0: int = 0) -> None:
+    """Stage 1 of attn_bwd_rope: D_t and the RoPE (cos, sin) table into the workspace."""
+    _check("o", o, 4)
+    _check("dout", dout, 4, o.device, o.dtype)
+    B, T, Hq, D = o.shape
+    wp, wb = _ws_args(workspace, o.device)
+    with torch.cuda.device(o.device):
+        st = lib().attn_bwd_rope_preprocess(o.data_ptr(), dout.data_ptr(), wp, wb, B, T, Hq, Hkv, D,
+                                            _dtype_code(o), float(base), int(pos0), _stream(o.device))
+    _raise(st, "attn_bwd_rope_preprocess")
+
+
+def attn_bwd_rope_main(q, k, v, lse, dout, workspace, dq, dk, dv, scale: float | None = None) -> None:
+    """Stage 2 of attn_bwd_rope in one launch: dv, and dq, dk rotated back by -phi."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    wp, wb = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_rope_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb,
+                                      B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd_rope_main")

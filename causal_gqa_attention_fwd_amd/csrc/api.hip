@@ -120,7 +120,12 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1 || !dtype_ok(dt)) return 0;
-    return ea::bwd_workspace_bytes(B, T, Hq, D);
+    return ea::bwd_workspace_bytes(B, T, Hq, D, false);
+}
+
+size_t attn_bwd_rope_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || !dtype_ok(dt)) return 0;
+    return ea::bwd_workspace_bytes(B, T, Hq, D, true);
 }
 
 }  // extern "C"
@@ -131,10 +136,16 @@ struct BwdSizes {
     size_t qb, kb, lseb, ws;
 };
 
-BwdSizes bwd_sizes(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
+BwdSizes bwd_sizes(int B, int T, int Hq, int Hkv, int D, ea_dtype dt, bool rope = false) {
     const size_t es = elem_size(dt);
     return BwdSizes{(size_t)B * T * Hq * D * es, (size_t)B * T * Hkv * D * es,
-                    (size_t)B * Hq * T * sizeof(float), ea::bwd_workspace_bytes(B, T, Hq, D)};
+                    (size_t)B * Hq * T * sizeof(float), ea::bwd_workspace_bytes(B, T, Hq, D, rope)};
+}
+
+ea_status check_rope_args(double base, int pos0, int T) {
+    if (!std::isfinite(base) || !(base > 1.0) || pos0 < 0) return EA_ERR_INVALID_ARG;
+    if ((long long)pos0 + T > (1LL << 31)) return EA_ERR_INVALID_ARG;
+    return EA_OK;
 }
 
 ea_status check_workspace(const void* ws, size_t bytes, size_t need) {
@@ -154,6 +165,66 @@ ea_status check_alias(const Range (&ins)[NI], const Range (&outs)[NO]) {
     return EA_OK;
 }
 
+ea_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
+                   ea_dtype dt, const ea::RopeArgs* rope, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (rope && (st = check_rope_args(rope->base, rope->pos0, T)) != EA_OK) return st;
+    for (const void* p : {q, k, v, o, static_cast<const void*>(lse), dout,
+                          static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt, rope != nullptr);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(o, z.qb),
+                         range(lse, z.lseb), range(dout, z.qb)};
+    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb), range(workspace, z.ws)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, T, Hq,
+                                        Hkv, D, scale, static_cast<ea::IoType>(dt), rope, stream));
+}
+
+ea_status pre_impl(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B,
+                   int T, int Hq, int Hkv, int D, ea_dtype dt, const ea::RopeArgs* rope,
+                   hipStream_t stream) {
+    if (!o || !dout || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, 1.0f, dt);
+    if (st != EA_OK) return st;
+    if (rope && (st = check_rope_args(rope->base, rope->pos0, T)) != EA_OK) return st;
+    if (!aligned16(o) || !aligned16(dout)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt, rope != nullptr);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(o, z.qb), range(dout, z.qb)};
+    const Range outs[] = {range(workspace, z.ws)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_pre(o, dout, workspace, B, T, Hq, D,
+                                       static_cast<ea::IoType>(dt), rope, stream));
+}
+
+ea_status main_impl(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                    size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
+                    ea_dtype dt, bool rope, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {q, k, v, static_cast<const void*>(lse), dout, static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt, rope);
+    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(lse, z.lseb),
+                         range(dout, z.qb), range(workspace, z.ws)};
+    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    return from_hip(ea::launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, const_cast<void*>(workspace),
+                                        B, T, Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), rope,
+                                        stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,37 +233,31 @@ ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
                    ea_dtype dt, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
-    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
-    if (st != EA_OK) return st;
-    for (const void* p : {q, k, v, o, static_cast<const void*>(lse), dout,
-                          static_cast<const void*>(dq), static_cast<const void*>(dk),
-                          static_cast<const void*>(dv)})
-        if (!aligned16(p)) return EA_ERR_ALIGN;
-    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
-    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
-    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(o, z.qb),
-                         range(lse, z.lseb), range(dout, z.qb)};
-    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb), range(workspace, z.ws)};
-    if ((st = check_alias(ins, outs)) != EA_OK) return st;
-    return from_hip(ea::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, T, Hq,
-                                        Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv,
+                    D, scale, dt, nullptr, stream);
+}
+
+ea_status attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv,
+                        int D, float scale, ea_dtype dt, double base, int pos0,
+                        hipStream_t stream) {
+    const ea::RopeArgs rope{base, pos0};
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv,
+                    D, scale, dt, &rope, stream);
 }
 
 ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
                               size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                               ea_dtype dt, hipStream_t stream) {
-    if (!o || !dout || !workspace) return EA_ERR_NULL;
-    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, 1.0f, dt);
-    if (st != EA_OK) return st;
-    if (!aligned16(o) || !aligned16(dout)) return EA_ERR_ALIGN;
-    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
-    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
-    const Range ins[] = {range(o, z.qb), range(dout, z.qb)};
-    const Range outs[] = {range(workspace, z.ws)};
-    if ((st = check_alias(ins, outs)) != EA_OK) return st;
-    return from_hip(ea::launch_bwd_pre(o, dout, workspace, B, T, Hq, D,
-                                       static_cast<ea::IoType>(dt), stream));
+    return pre_impl(o, dout, workspace, workspace_bytes, B, T, Hq, Hkv, D, dt, nullptr, stream);
+}
+
+ea_status attn_bwd_rope_preprocess(const void* o, const void* dout, void* workspace,
+                                   size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                                   ea_dtype dt, double base, int pos0, hipStream_t stream) {
+    const ea::RopeArgs rope{base, pos0};
+    return pre_impl(o, dout, workspace, workspace_bytes, B, T, Hq, Hkv, D, dt, &rope, stream);
 }
 
 ea_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
@@ -219,20 +284,16 @@ ea_status attn_bwd_main(const void* q, const void* k, const void* v, const float
                         const void* dout, void* dq, void* dk, void* dv, const void* workspace,
                         size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                         float scale, ea_dtype dt, hipStream_t stream) {
-    if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
-    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
-    if (st != EA_OK) return st;
-    for (const void* p : {q, k, v, static_cast<const void*>(lse), dout, static_cast<const void*>(dq),
-                          static_cast<const void*>(dk), static_cast<const void*>(dv)})
-        if (!aligned16(p)) return EA_ERR_ALIGN;
-    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
-    if ((st = check_workspace(workspace, workspace_bytes, z.ws)) != EA_OK) return st;
-    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(lse, z.lseb),
-                         range(dout, z.qb), range(workspace, z.ws)};
-    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb)};
-    if ((st = check_alias(ins, outs)) != EA_OK) return st;
-    return from_hip(ea::launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, const_cast<void*>(workspace),
-                                        B, T, Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
+    return main_impl(q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, D,
+                     scale, dt, false, stream);
+}
+
+ea_status attn_bwd_rope_main(const void* q, const void* k, const void* v, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                             float scale, ea_dtype dt, hipStream_t stream) {
+    return main_impl(q, k, v, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, D,
+                     scale, dt, true, stream);
 }
 
 ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,

@@ -36,11 +36,25 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------------------
 // 1. D_t = sum_d dO * O per row.
 // ---------------------------------------------------------------------------------------
+// Blocks past dt_blocks fill the RoPE table instead: entry (t, i) = (cos, sin) of the angle of
+// pair i at position pos0 + t, [T][D/2] float2, for the inverse RoPE applied on the stores of
+// dQ and dK (absent when cs is null).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
                                                       const T* __restrict__ dout,
                                                       float* __restrict__ dt, long long nrows,
-                                                      int T_, int Hq) {
+                                                      int T_, int Hq, long long dt_blocks,
+                                                      float* __restrict__ cs, int pos0, RopeFreq f) {
+    if ((long long)blockIdx.x >= dt_blocks) {
+        const long long u = ((long long)blockIdx.x - dt_blocks) * 256 + threadIdx.x;
+        if (u < (long long)T_ * (D / 2)) {
+            const int t = (int)(u / (D / 2)), i = (int)(u % (D / 2));
+            float c, sn;
+            rope_cos_sin((double)pos0 + (double)t, f.theta[i], &c, &sn);
+            reinterpret_cast<float2*>(cs)[u] = make_float2(c, sn);
+        }
+        return;
+    }
     constexpr int EPC = 16 / sizeof(T);
     constexpr int LPR = D / EPC;  // lanes per row (4 .. 32)
     const int tid = threadIdx.x;
@@ -82,6 +96,7 @@ struct BwdArgs {
     int roles;        // 1: dK/dV only, 2: dQ only, 3: both in one launch
     float sl2;        // scale * log2(e)
     float scale;
+    const float* rope_cs;  // (cos, sin) per (t, pair) for the inverse RoPE on dQ / dK, or null
 };
 
 // ---------------------------------------------------------------------------------------
@@ -308,6 +323,22 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         }
     }
     if (qh != 0) return;
+    if (a.rope_cs != nullptr) {
+        // dK_raw = R(-phi) dK.  Pair (d, d+1) of a key sits in lanes (l, l ^ 1) of one register.
+        const float sgn = (l32 & 1) ? -1.0f : 1.0f;
+        const float2* tab = reinterpret_cast<const float2*>(a.rope_cs);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = min(j * BN + kh * 32 + acc_row(r, half), a.T - 1);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const float x = dkacc[db][r];
+                const float y = __shfl_xor(x, 1, 64);
+                const float2 w = tab[(long long)key * (D / 2) + ((db * 32 + l32) >> 1)];
+                dkacc[db][r] = x * w.x + sgn * (y * w.y);
+            }
+        }
+    }
     T* __restrict__ dkp = static_cast<T*>(a.dk);
     T* __restrict__ dvp = static_cast<T*>(a.dv);
 #pragma unroll
@@ -510,6 +541,24 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     }
 
     if (!active || tq >= a.T) return;
+    if (a.rope_cs != nullptr) {
+        // dQ_raw = R(-phi) dQ.  Pair (d, d+1) sits in registers (r, r+1), r even, of this lane;
+        // one 16-byte table read gives (cos, sin) of two consecutive pairs.
+        const float4* cs = reinterpret_cast<const float4*>(a.rope_cs + (long long)tq * D);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const float4 w = cs[(db * 32 + 8 * a4 + 4 * half) / 4];
+                f32x16& x = dqacc[db];
+                const int r = 4 * a4;
+                const float x0 = x[r], x1 = x[r + 1], x2 = x[r + 2], x3 = x[r + 3];
+                x[r] = x0 * w.x + x1 * w.y;
+                x[r + 1] = x1 * w.x - x0 * w.y;
+                x[r + 2] = x2 * w.z + x3 * w.w;
+                x[r + 3] = x3 * w.z - x2 * w.w;
+            }
+    }
     T* __restrict__ dqp = static_cast<T*>(a.dq);
     T* row = dqp + (((long long)b * a.T + tq) * a.Hq + head) * D;
 #pragma unroll
@@ -597,14 +646,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
 
 template <typename T, int D>
 hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, int seq, int Hq,
-                        hipStream_t stream) {
+                        float* cs, const RopeArgs* rope, hipStream_t stream) {
     const long long nrows = (long long)B * seq * Hq;
     constexpr int LPR = D / (16 / sizeof(T));
     const long long rows_per_block = 256 / LPR;
-    const long long blocks = (nrows + rows_per_block - 1) / rows_per_block;
+    const long long dt_blocks = (nrows + rows_per_block - 1) / rows_per_block;
+    RopeFreq f;
+    fill_rope_freq(&f, D, rope ? rope->base : 2.0);
+    const long long tab_blocks = rope ? ((long long)seq * (D / 2) + 255) / 256 : 0;
+    const long long blocks = dt_blocks + tab_blocks;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const T*>(o), static_cast<const T*>(dout), dtbuf, nrows, seq, Hq);
+                       static_cast<const T*>(o), static_cast<const T*>(dout), dtbuf, nrows, seq, Hq,
+                       dt_blocks, cs, rope ? rope->pos0 : 0, f);
     return hipGetLastError();
 }
 
@@ -691,10 +745,14 @@ hipError_t launch_bwd_roles(const BwdArgs& a, int D, int roles, hipStream_t stre
 }
 
 float* ws_dt(void* ws) { return static_cast<float*>(ws); }
+size_t dt_bytes(int B, int T, int Hq) { return align256((size_t)B * Hq * T * sizeof(float)); }
+float* ws_rope(void* ws, int B, int T, int Hq) {
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + dt_bytes(B, T, Hq));
+}
 
 BwdArgs make_args(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, void* workspace, int B, int T, int Hq, int Hkv,
-                  float scale) {
+                  float scale, bool rope = false) {
     BwdArgs a{};
     a.q = q;
     a.k = k;
@@ -711,27 +769,28 @@ BwdArgs make_args(const void* q, const void* k, const void* v, const float* lse,
     a.Hkv = Hkv;
     a.sl2 = scale * kLog2e;
     a.scale = scale;
+    a.rope_cs = rope ? ws_rope(workspace, B, T, Hq) : nullptr;
     return a;
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int T, int Hq, int D) {
-    (void)D;
-    return align256((size_t)B * Hq * T * sizeof(float));
+size_t bwd_workspace_bytes(int B, int T, int Hq, int D, bool rope) {
+    return dt_bytes(B, T, Hq) + (rope ? align256((size_t)T * (D / 2) * 2 * sizeof(float)) : 0);
 }
 
 hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
-                          int D, IoType dt, hipStream_t stream) {
+                          int D, IoType dt, const RopeArgs* rope, hipStream_t stream) {
     float* dtb = ws_dt(workspace);
+    float* cs = rope ? ws_rope(workspace, B, T, Hq) : nullptr;
     if (dt == kF32) {
-        if (D == 32) return launch_pre_t<float, 32>(o, dout, dtb, B, T, Hq, stream);
-        if (D == 64) return launch_pre_t<float, 64>(o, dout, dtb, B, T, Hq, stream);
-        return launch_pre_t<float, 128>(o, dout, dtb, B, T, Hq, stream);
+        if (D == 32) return launch_pre_t<float, 32>(o, dout, dtb, B, T, Hq, cs, rope, stream);
+        if (D == 64) return launch_pre_t<float, 64>(o, dout, dtb, B, T, Hq, cs, rope, stream);
+        return launch_pre_t<float, 128>(o, dout, dtb, B, T, Hq, cs, rope, stream);
     }
-    if (D == 32) return launch_pre_t<bf16, 32>(o, dout, dtb, B, T, Hq, stream);
-    if (D == 64) return launch_pre_t<bf16, 64>(o, dout, dtb, B, T, Hq, stream);
-    return launch_pre_t<bf16, 128>(o, dout, dtb, B, T, Hq, stream);
+    if (D == 32) return launch_pre_t<bf16, 32>(o, dout, dtb, B, T, Hq, cs, rope, stream);
+    if (D == 64) return launch_pre_t<bf16, 64>(o, dout, dtb, B, T, Hq, cs, rope, stream);
+    return launch_pre_t<bf16, 128>(o, dout, dtb, B, T, Hq, cs, rope, stream);
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
@@ -750,19 +809,20 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
 
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
-                           int T, int Hq, int Hkv, int D, float scale, IoType dt,
+                           int T, int Hq, int Hkv, int D, float scale, IoType dt, bool rope,
                            hipStream_t stream) {
-    const BwdArgs a = make_args(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, scale);
+    const BwdArgs a = make_args(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, scale, rope);
     return dt == kF32 ? launch_bwd_roles<float>(a, D, 3, stream) : launch_bwd_roles<bf16>(a, D, 3, stream);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
-                           IoType dt, hipStream_t stream) {
-    hipError_t e = launch_bwd_pre(o, dout, workspace, B, T, Hq, D, dt, stream);
+                           IoType dt, const RopeArgs* rope, hipStream_t stream) {
+    hipError_t e = launch_bwd_pre(o, dout, workspace, B, T, Hq, D, dt, rope, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt, stream);
+    return launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt,
+                           rope != nullptr, stream);
 }
 
 }  // namespace ea

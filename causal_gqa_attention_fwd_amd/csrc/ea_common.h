@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace ea {
 
 typedef __bf16 bf16;
@@ -187,6 +189,29 @@ __device__ inline f32x16 zero_acc() {
 
 __device__ inline float xor_shfl32(float x) {
     return __shfl_xor(x, 32, 64);
+}
+
+// RoPE frequencies theta_i = base^(-2i/D), i < D/2 <= 128, computed on the host in double
+// and passed by value to the kernels that rotate.
+struct RopeFreq {
+    double theta[128];
+};
+
+inline void fill_rope_freq(RopeFreq* f, int D, double base) {
+    for (int i = 0; i < 128; ++i) f->theta[i] = (i < D / 2) ? pow(base, -2.0 * (double)i / (double)D) : 0.0;
+}
+
+// cos and sin of the RoPE angle phi = pos * theta: phi is formed and reduced modulo 2*pi in
+// double (two-term 2*pi), and the reduced angle, |r| <= pi, goes to fp32 sincos.
+__device__ inline void rope_cos_sin(double pos, double theta, float* c, float* s) {
+    constexpr double kTwoPiHi = 6.283185307179586;       // nearest double to 2*pi
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double phi = pos * theta;
+    const double n = rint(phi * kInvTwoPi);
+    double r = fma(-n, kTwoPiHi, phi);
+    r = fma(-n, kTwoPiLo, r);
+    sincosf((float)r, s, c);
 }
 
 }  // namespace ea

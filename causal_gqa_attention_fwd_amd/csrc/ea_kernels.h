@@ -8,6 +8,12 @@ namespace ea {
 
 enum IoType { kF32 = 0, kBF16 = 1 };
 
+// Inverse RoPE fused into the backward: gradients are returned for the pre-rotation Q and K.
+struct RopeArgs {
+    double base;
+    int pos0;
+};
+
 // RoPE of x [B, T, H, D] into y; see rope_apply in euler_attn.h.
 hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoType dt,
                        double base, int pos0, int inverse, hipStream_t stream);
@@ -22,31 +28,33 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
                            hipStream_t stream);
 
-// Workspace of the backward: D_t = sum_d dO * O as fp32 [B, Hq, T], 256-byte aligned.
-size_t bwd_workspace_bytes(int B, int T, int Hq, int D);
+// Workspace of the backward: D_t = sum_d dO * O as fp32 [B, Hq, T], 256-byte aligned; with
+// rope, then the (cos, sin) table of the inverse RoPE, fp32 [T, D/2, 2], 256-byte aligned.
+size_t bwd_workspace_bytes(int B, int T, int Hq, int D, bool rope);
 
 // Backward stages (their composition is launch_attn_bwd):
-//   pre:  D_t into the workspace;
+//   pre:  D_t (and, with rope, the RoPE table) into the workspace;
 //   dkdv: dk, dv (group-summed) from q, k, v, lse, dout and D_t;
 //   dq:   dq from q, k, v, lse, dout and D_t (independent of dkdv).
 hipError_t launch_bwd_pre(const void* o, const void* dout, void* workspace, int B, int T, int Hq,
-                          int D, IoType dt, hipStream_t stream);
+                          int D, IoType dt, const RopeArgs* rope, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dk, void* dv, void* workspace, int B, int T,
                            int Hq, int Hkv, int D, float scale, IoType dt, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                          const void* dout, void* dq, void* workspace, int B, int T, int Hq,
                          int Hkv, int D, float scale, IoType dt, hipStream_t stream);
-// dkdv and dq in one launch (the two roles' workgroups interleaved, heaviest first).
+// dkdv and dq in one launch (the two roles' workgroups interleaved, heaviest first); with
+// rope, dq and dk are rotated by -phi (table from pre) before they are stored.
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
-                           int T, int Hq, int Hkv, int D, float scale, IoType dt,
+                           int T, int Hq, int Hkv, int D, float scale, IoType dt, bool rope,
                            hipStream_t stream);
 
-// Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above.
+// Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above (rope may be null).
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
-                           IoType dt, hipStream_t stream);
+                           IoType dt, const RopeArgs* rope, hipStream_t stream);
 
 }  // namespace ea

@@ -19,13 +19,6 @@
 namespace ea {
 namespace {
 
-struct RopeFreq {
-    double theta[128];  // base^(-2i/D), i < D/2 <= 128
-};
-
-constexpr double kTwoPiHi = 6.283185307179586;       // nearest double to 2*pi
-constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189535;
 constexpr int kHeadsPerThread = 4;
 
 // Up to two tensors [B, T, H_k, D] in one launch (Q and K, or dQ and dK): units
@@ -38,52 +31,60 @@ struct RopeJob {
     long long n0, ntot;
 };
 
-template <typename T>
+// I: unsigned index type of the unit decomposition (32-bit whenever the units fit).
+template <typename T, typename I>
 __global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int D, int pos0,
                                                    int inverse, RopeFreq f) {
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int PPC = EPC / 2;         // pairs per chunk
-    long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (u >= job.ntot) return;
-    const int which = u < job.n0 ? 0 : 1;
-    if (which) u -= job.n0;
+    I u = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
+    if (u >= (I)job.ntot) return;
+    const int which = u < (I)job.n0 ? 0 : 1;
+    if (which) u -= (I)job.n0;
     const T* x = job.x[which];
     T* y = job.y[which];
     const int H = job.H[which];
-    const int cpr = D / EPC;  // chunks per row
-    const int nhb = (H + kHeadsPerThread - 1) / kHeadsPerThread;
+    const I cpr = (I)(D / EPC);  // chunks per row
+    const I nhb = (I)((H + kHeadsPerThread - 1) / kHeadsPerThread);
     const int c = (int)(u % cpr);
-    const long long rest = u / cpr;
+    const I rest = u / cpr;
     const int hb = (int)(rest % nhb);
-    const long long bt = rest / nhb;
+    const long long bt = (long long)(rest / nhb);
     const int t = (int)(bt % seq);
     const double pos = (double)pos0 + (double)t;
+    const int h0 = hb * kHeadsPerThread;
+    const int nh = min(H - h0, kHeadsPerThread);
+    const long long off0 = (bt * H + h0) * (long long)D + (long long)c * EPC;
+
+    // Every load of this thread is issued before any store: its chunks are disjoint from
+    // every other thread's, so this is also correct in place, and the loads overlap the
+    // angle computation instead of waiting behind each other's stores.
+    Vec16<T> v[kHeadsPerThread];
+#pragma unroll
+    for (int k = 0; k < kHeadsPerThread; ++k)
+        if (k < nh) v[k] = ld16(x + off0 + (long long)k * D);
 
     float cs[PPC], sn[PPC];
 #pragma unroll
     for (int p = 0; p < PPC; ++p) {
-        const double phi = pos * f.theta[c * PPC + p];
-        const double n = rint(phi * kInvTwoPi);
-        double r = fma(-n, kTwoPiHi, phi);
-        r = fma(-n, kTwoPiLo, r);
         float s, co;
-        sincosf((float)r, &s, &co);
+        rope_cos_sin(pos, f.theta[c * PPC + p], &co, &s);
         cs[p] = co;
         sn[p] = inverse ? -s : s;
     }
-    const int h_end = min(H, (hb + 1) * kHeadsPerThread);
-    for (int h = hb * kHeadsPerThread; h < h_end; ++h) {
-        const long long off = (bt * H + h) * (long long)D + (long long)c * EPC;
-        Vec16<T> v = ld16(x + off);
-        Vec16<T> w;
 #pragma unroll
-        for (int p = 0; p < PPC; ++p) {
-            const float x0 = to_f32(v.get(2 * p));
-            const float x1 = to_f32(v.get(2 * p + 1));
-            w.set(2 * p, from_f32<T>(x0 * cs[p] - x1 * sn[p]));
-            w.set(2 * p + 1, from_f32<T>(x0 * sn[p] + x1 * cs[p]));
+    for (int k = 0; k < kHeadsPerThread; ++k) {
+        if (k < nh) {
+            Vec16<T> w;
+#pragma unroll
+            for (int p = 0; p < PPC; ++p) {
+                const float x0 = to_f32(v[k].get(2 * p));
+                const float x1 = to_f32(v[k].get(2 * p + 1));
+                w.set(2 * p, from_f32<T>(x0 * cs[p] - x1 * sn[p]));
+                w.set(2 * p + 1, from_f32<T>(x0 * sn[p] + x1 * cs[p]));
+            }
+            st16(y + off0 + (long long)k * D, w);
         }
-        st16(y + off, w);
     }
 }
 
@@ -92,8 +93,7 @@ hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void*
                          int seq, int D, double base, int pos0, int inverse, hipStream_t stream) {
     constexpr int EPC = 16 / sizeof(T);
     RopeFreq f;
-    for (int i = 0; i < D / 2; ++i) f.theta[i] = std::pow(base, -2.0 * (double)i / (double)D);
-    for (int i = D / 2; i < 128; ++i) f.theta[i] = 0.0;
+    fill_rope_freq(&f, D, base);
     RopeJob<T> job;
     job.x[0] = static_cast<const T*>(x0);
     job.y[0] = static_cast<T*>(y0);
@@ -109,8 +109,12 @@ hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void*
     const int threads = 256;
     const long long blocks = (job.ntot + threads - 1) / threads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(rope_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, stream, job, seq, D,
-                       pos0, inverse, f);
+    if (blocks * threads <= 0xffffffffLL)
+        hipLaunchKernelGGL((rope_kernel<T, uint32_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           job, seq, D, pos0, inverse, f);
+    else
+        hipLaunchKernelGGL((rope_kernel<T, uint64_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           job, seq, D, pos0, inverse, f);
     return hipGetLastError();
 }
 

@@ -144,6 +144,35 @@ ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* 
                       int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
                       hipStream_t stream);
 
+/*
+ * The backward with the RoPE backward fused in.  The pages rotate queries and keys before the
+ * attention ("Show HN: NanoEuler", section 2) and check RoPE's backward with the rest of the
+ * model's gradients (section 4); the backward of the rotation is the rotation by -phi.
+ * attn_bwd_rope takes the same inputs as attn_bwd (q and k are the rotated tensors that
+ * attn_fwd received) and returns dq and dk with respect to the tensors BEFORE rope_apply,
+ * i.e. what attn_bwd followed by rope_apply(inverse = 1) on dq and dk with the same base
+ * and pos0 computes, but in one pass: the rotation is applied to the float32 gradients just
+ * before they are rounded and stored (one rounding instead of two).  dv is unchanged.
+ * The workspace (attn_bwd_rope_workspace_size bytes, 256-byte aligned) holds D_t as for
+ * attn_bwd followed by a float32 (cos, sin) table [T, D/2, 2] of the rotation angles,
+ * computed like rope_apply's.  Stages: attn_bwd_rope is attn_bwd_rope_preprocess (D_t and
+ * the table) followed by attn_bwd_rope_main.  Errors: as attn_bwd, plus base <= 1 or not
+ * finite, pos0 < 0 or pos0 + T > 2^31 (EA_ERR_INVALID_ARG).
+ */
+size_t attn_bwd_rope_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt);
+ea_status attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv,
+                        int D, float scale, ea_dtype dt, double base, int pos0,
+                        hipStream_t stream);
+ea_status attn_bwd_rope_preprocess(const void* o, const void* dout, void* workspace,
+                                   size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                                   ea_dtype dt, double base, int pos0, hipStream_t stream);
+ea_status attn_bwd_rope_main(const void* q, const void* k, const void* v, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
+                             float scale, ea_dtype dt, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* euler_attn_status_string(ea_status s);
 

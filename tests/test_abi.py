@@ -38,8 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
-              "euler_attn_status_string", "euler_attn_version"):
+    for n in ("rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_rope",
+              "attn_bwd_rope_workspace_size", "euler_attn_status_string", "euler_attn_version"):
         assert n in names
 
 
@@ -172,6 +172,48 @@ def test_bwd_stage_validation(L):
     assert dq(wb=16) == WS
     assert dq(dq=fake(0) + 256) == ALIAS
     assert dq(dq=fake(6)) == ALIAS
+
+
+def test_bwd_rope_workspace_size(L):
+    # D_t as for attn_bwd, then the fp32 (cos, sin) table [T, D/2, 2], each rounded to 256 bytes.
+    def up(x):
+        return (x + 255) // 256 * 256
+    for (B, T, Hq, Hkv, D) in ((4, 1024, 12, 4, 64), (1, 3, 1, 1, 32), (8, 4096, 32, 8, 128)):
+        assert L.attn_bwd_rope_workspace_size(B, T, Hq, Hkv, D, BF16) == \
+            L.attn_bwd_workspace_size(B, T, Hq, Hkv, D, BF16) + up(T * D * 4)
+    assert L.attn_bwd_rope_workspace_size(1, 4, 3, 2, 32, BF16) == 0
+
+
+def test_bwd_rope_validation(L):
+    ws = L.attn_bwd_rope_workspace_size(2, 16, 4, 2, 64, BF16)
+
+    def br(q=fake(0), dq=fake(6), dk=fake(7), w=fake(9), wb=ws, base=1e4, pos0=0, D=64, T=16):
+        return L.attn_bwd_rope(q, fake(1), fake(2), fake(3), fake(4), fake(5), dq, dk, fake(8), w, wb,
+                               2, T, 4, 2, D, 0.125, BF16, base, pos0, None)
+    assert br(q=None) == NULL
+    for kw in (dict(base=1.0), dict(base=0.5), dict(base=float("nan")), dict(base=float("inf")),
+               dict(pos0=-1), dict(pos0=(1 << 31) - 8)):
+        assert br(**kw) == INVALID, kw
+    assert br(D=96) == UNSUP
+    # the plain backward's workspace is too small for the table
+    assert br(wb=L.attn_bwd_workspace_size(2, 16, 4, 2, 64, BF16)) == WS
+    assert br(wb=ws - 1) == WS
+    assert br(w=fake(9) + 128) == ALIGN
+    assert br(dk=fake(6)) == ALIAS
+    assert br(w=fake(7)) == ALIAS
+    pre = lambda w=fake(2), wb=ws, base=1e4, pos0=0: L.attn_bwd_rope_preprocess(  # noqa
+        fake(0), fake(1), w, wb, 2, 16, 4, 2, 64, BF16, base, pos0, None)
+    assert pre(w=None) == NULL
+    assert pre(base=1.0) == INVALID
+    assert pre(pos0=-3) == INVALID
+    assert pre(wb=ws - 1) == WS
+    assert pre(w=fake(1)) == ALIAS
+    mn = lambda dq=fake(5), w=fake(8), wb=ws: L.attn_bwd_rope_main(  # noqa
+        fake(0), fake(1), fake(2), fake(3), fake(4), dq, fake(6), fake(7), w, wb, 2, 16, 4, 2, 64, 0.1,
+        BF16, None)
+    assert mn(dq=None) == NULL
+    assert mn(wb=L.attn_bwd_workspace_size(2, 16, 4, 2, 64, BF16)) == WS
+    assert mn(dq=fake(8)) == ALIAS
 
 
 def test_binding_refuses_cpu_tensors():
