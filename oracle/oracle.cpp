@@ -122,6 +122,57 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o
     return 0;
 }
 
+// Causal GQA attention of Tq new query rows against a cache of Tk >= Tq key/value rows
+// (generation with a KV cache: "Show HN: NanoEuler", section 2 -- the multi-token prediction
+// heads used for speculative decoding -- and its key points -- the interactive chat REPL).  The queries are the last Tq positions of
+// the sequence, so query row i sits at absolute position (Tk - Tq) + i and, causally, sees the
+// keys s <= (Tk - Tq) + i.  Per (b, h, i), kv = h / g, off = Tk - Tq:
+//   S_is  = scale * sum_d Q[b,i,h,d] K[b,s,kv,d]       for s <= off + i
+//   O_i   = sum_s softmax_s(S_i.) V[b,s,kv,:],  LSE_i = log sum_s exp(S_is)
+// Layouts: q, o [B, Tq, Hq, D]; k, v [B, Tk, Hkv, D]; lse [B, Hq, Tq].  With Tq = Tk this is
+// the causal self-attention above.  Two passes per row, as oracle_attn_fwd.
+// Returns 0, 1 when Hq is not a multiple of Hkv, 2 when Tq > Tk.
+int oracle_attn_fwd_kv(const double* q, const double* k, const double* v, double* o, double* lse,
+                       long B, long Tq, long Tk, long Hq, long Hkv, long D, double scale) {
+    if (Hkv <= 0 || Hq % Hkv != 0) return 1;
+    if (Tq > Tk) return 2;
+    const long g = Hq / Hkv;
+    const long off = Tk - Tq;
+#pragma omp parallel
+    {
+        std::vector<double> srow(Tk > 0 ? Tk : 1);
+#pragma omp for collapse(3) schedule(dynamic, 8)
+        for (long b = 0; b < B; ++b) {
+            for (long h = 0; h < Hq; ++h) {
+                for (long i = 0; i < Tq; ++i) {
+                    const long kv = h / g;
+                    const long last = off + i;  // last visible key
+                    const double* qi = q + q_index(b, i, h, 0, Tq, Hq, D);
+                    double m = -INFINITY;
+                    for (long s = 0; s <= last; ++s) {
+                        const double* ks = k + q_index(b, s, kv, 0, Tk, Hkv, D);
+                        double acc = 0.0;
+                        for (long d = 0; d < D; ++d) acc += qi[d] * ks[d];
+                        srow[s] = scale * acc;
+                        if (srow[s] > m) m = srow[s];
+                    }
+                    double z = 0.0;
+                    for (long s = 0; s <= last; ++s) z += std::exp(srow[s] - m);
+                    double* oi = o + q_index(b, i, h, 0, Tq, Hq, D);
+                    for (long d = 0; d < D; ++d) oi[d] = 0.0;
+                    for (long s = 0; s <= last; ++s) {
+                        const double p = std::exp(srow[s] - m) / z;
+                        const double* vs = v + q_index(b, s, kv, 0, Tk, Hkv, D);
+                        for (long d = 0; d < D; ++d) oi[d] += p * vs[d];
+                    }
+                    lse[(b * Hq + h) * Tq + i] = m + std::log(z);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 // Causal GQA attention backward, analytic, from the fully materialised masked softmax of
 // one (b, h) at a time.  Given dO = dL/dO:
 //   dP_ts = dO_t . V_s

@@ -14,6 +14,10 @@ What each function computes, and the passage it follows, is stated at the C defi
  * ``attn_bwd``  -- the analytic gradients of L = sum(dO * O) with respect to the post-RoPE
                     Q, K and V, dK/dV summed over each query-head group.
  * ``grads_raw`` -- the end-to-end gradients with respect to the pre-RoPE Q and K.
+ * ``attn_fwd_kv`` -- the same causal attention for Tq new query rows against a cache of
+                    Tk >= Tq keys (generation with a KV cache: "Show HN: NanoEuler", section 2,
+                    speculative decoding with the MTP heads, and the chat REPL of its key
+                    points): query row i sits at position Tk - Tq + i.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms,
 invariants, brute force, a library special case and central finite differences.
@@ -58,6 +62,8 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
         lib.oracle_attn_fwd.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
+        lib.oracle_attn_fwd_kv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, L, ctypes.c_double]
+        lib.oracle_attn_fwd_kv.restype = ctypes.c_int
         lib.oracle_attn_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -117,6 +123,27 @@ def attn_fwd(q, k, v, scale: float | None = None):
                                  float(scale))
     if rc != 0:
         raise ValueError("attn_fwd: bad head counts")
+    return o, lse
+
+
+def attn_fwd_kv(q, k, v, scale: float | None = None):
+    """Causal GQA attention of q [B,Tq,Hq,D] against a cache k, v [B,Tk,Hkv,D], Tk >= Tq; query
+    row i sits at position Tk - Tq + i -> (O [B,Tq,Hq,D], LSE [B,Hq,Tq]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Tq,Hq,D] and k, v [B,Tk,Hkv,D]")
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or Hkv < 1 or Hq % Hkv != 0 or Tq > Tk:
+        raise ValueError("attn_fwd_kv: bad shapes")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, Tq), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Tq, Tk, Hq, Hkv, D,
+                                    float(scale))
+    if rc != 0:
+        raise ValueError("attn_fwd_kv: bad shapes")
     return o, lse
 
 
