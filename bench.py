@@ -189,6 +189,44 @@ def roofline_for(w, kern_us, name):
             "algorithmic_bytes_per_launch": alg["bytes"], "avg_launch_us": round(kern_us[name], 2)}
 
 
+def time_decode(name, steps, warmup, torch, ea, W):
+    """attn_decode on a decode workload: average microseconds per call over `steps` calls with
+    inputs resident in HBM, and the algorithmic HBM rate (q and the K/V cache read, o and lse
+    written) against the 8 TB/s peak."""
+    w = W.DECODE_WORKLOADS[name]
+    log("[bench] decode workload %s" % name)
+    inp = W.make_decode_inputs(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Tq), device=dev, dtype=torch.float32)
+    L = ea.lib()
+    dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+    nws = max(256, L.attn_decode_workspace_size(w.B, w.Tq, w.Tk, w.Hq, w.Hkv, w.D, dtc))
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nws,
+            w.B, w.Tq, w.Tk, w.Hq, w.Hkv, w.D, 1.0 / (w.D ** 0.5), dtc, stream)
+    for _ in range(warmup):
+        if L.attn_decode(*args) != 0:
+            raise RuntimeError("attn_decode failed")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        L.attn_decode(*args)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1000.0 / steps
+    gbs = w.hbm_bytes() / (us * 1e-6) / 1e9
+    return {"config": w.describe(), "calls": steps, "us_per_call": round(us, 2),
+            "hbm_bytes_per_call": w.hbm_bytes(),
+            "roofline": {"kernel": "attn_decode (partial + merge launches)", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def cpu_baseline(w, W):
     """The oracle (plain float64 C++, OpenMP) on the host cores: one whole step of the same
     workload (RoPE on Q and K, forward, analytic backward, inverse RoPE on dQ and dK)."""
@@ -229,6 +267,9 @@ def main() -> int:
     ap.add_argument("--extra", default="long_t8192",
                     help="comma-separated extra workloads timed the same way (reported under 'extra')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", default="decode_b8_tk8192,decode_mtp4_b16_tk1024",
+                    help="comma-separated decode workloads (attn_decode against a KV cache) reported "
+                         "under 'decode'; empty to skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -293,6 +334,8 @@ def main() -> int:
                        "frac_of_peak": round(tf / PEAK_TFLOPS[we.dtype], 4), "steps": steps,
                        "kernel_us": {k: round(v, 2) for k, v in ke.items()}}
     out["extra"] = extra
+    out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
+                     for name in [x for x in args.decode.split(",") if x]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on host cores")
         out["cpu_baseline"] = cpu_baseline(w, W)

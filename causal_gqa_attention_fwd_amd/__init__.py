@@ -11,6 +11,7 @@ built, or the tensors are not on a ROCm device, the calls raise.
     attn_bwd(q, k, v, o, lse, dout, scale=None, ...)         -> (dq, dk, dv)
     attn_bwd_rope(q, k, v, o, lse, dout, base=1e4, pos0=0, ...)
                          -> (dq, dk, dv) with dq, dk for the tensors before RoPE
+    attn_decode(q, k_cache, v_cache, scale=None, ...)         -> (o, lse) for the last Tq rows
 
 Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
 dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
@@ -25,7 +26,7 @@ import torch
 
 __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
-           "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_rope_preprocess.restype = ci
     L.attn_bwd_rope_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_bwd_rope_main.restype = ci
+    L.attn_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    L.attn_decode_workspace_size.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_decode.restype = ci
     L.euler_attn_status_string.argtypes = [ci]
     L.euler_attn_status_string.restype = ctypes.c_char_p
     L.euler_attn_version.argtypes = []
@@ -327,3 +332,37 @@ def attn_bwd_rope_main(q, k, v, lse, dout, workspace, dq, dk, dv, scale: float |
                                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wb,
                                       B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
     _raise(st, "attn_bwd_rope_main")
+
+
+def attn_decode_workspace_size(B: int, Tq: int, Tk: int, Hq: int, Hkv: int, D: int, dtype=torch.bfloat16) -> int:
+    code = EA_F32 if dtype == torch.float32 else EA_BF16
+    return int(lib().attn_decode_workspace_size(B, Tq, Tk, Hq, Hkv, D, code))
+
+
+def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """Attention of q [B,Tq,Hq,D] (the last Tq positions) against the cache k, v [B,Tk,Hkv,D];
+    returns (o [B,Tq,Hq,D], lse [B,Hq,Tq] float32)."""
+    _check("q", q, 4)
+    _check("k", k, 4, q.device, q.dtype)
+    _check("v", v, 4, q.device, q.dtype)
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Tk, Hkv, D] matching q [B, Tq, Hq, D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    _check("out", o, 4, q.device, q.dtype)
+    l = torch.empty((B, Hq, Tq), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check("lse", l, 3, q.device, torch.float32)
+    need = int(lib().attn_decode_workspace_size(B, Tq, Tk, Hq, Hkv, D, _dtype_code(q)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    wp, wb = _ws_args(workspace, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), wp, wb,
+                               B, Tq, Tk, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_decode")
+    return o, l

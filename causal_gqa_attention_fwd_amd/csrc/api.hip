@@ -123,6 +123,39 @@ size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt
     return ea::bwd_workspace_bytes(B, T, Hq, D, false);
 }
 
+size_t attn_decode_workspace_size(int B, int Tq, int Tk, int Hq, int Hkv, int D, ea_dtype dt) {
+    if (B < 1 || Tq < 1 || Tk < Tq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !dtype_ok(dt)) return 0;
+    if (D != 32 && D != 64 && D != 128) return 0;
+    return ea::decode_workspace_bytes(B, Tq, Tk, Hq, Hkv, D);
+}
+
+ea_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int Tq, int Tk, int Hq,
+                      int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !workspace) return EA_ERR_NULL;
+    if (Tq < 1 || Tk < Tq) return EA_ERR_INVALID_ARG;
+    ea_status st = check_attn_sizes(B, Tk, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return EA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EA_ERR_ALIGN;
+    const size_t need = ea::decode_workspace_bytes(B, Tq, Tk, Hq, Hkv, D);
+    if (workspace_bytes < need) return EA_ERR_WORKSPACE;
+    const size_t es = elem_size(dt);
+    const Range rq = range(q, (size_t)B * Tq * Hq * D * es);
+    const Range rk = range(k, (size_t)B * Tk * Hkv * D * es);
+    const Range rv = range(v, (size_t)B * Tk * Hkv * D * es);
+    const Range ro = range(o, (size_t)B * Tq * Hq * D * es);
+    const Range rl = range(lse, (size_t)B * Hq * Tq * sizeof(float));
+    const Range rw = range(workspace, need);
+    for (Range out : {ro, rl, rw})
+        for (Range in : {rq, rk, rv})
+            if (overlap(out, in)) return EA_ERR_ALIAS;
+    if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw)) return EA_ERR_ALIAS;
+    return from_hip(ea::launch_attn_decode(q, k, v, o, lse, workspace, B, Tq, Tk, Hq, Hkv, D, scale,
+                                           static_cast<ea::IoType>(dt), stream));
+}
+
 size_t attn_bwd_rope_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 2 || !dtype_ok(dt)) return 0;
     return ea::bwd_workspace_bytes(B, T, Hq, D, true);

@@ -1,0 +1,345 @@
+// attn_decode.hip -- causal GQA attention of a few new query rows against a KV cache on
+// gfx950 (attn_decode).
+//
+// What it computes: the causal attention of the pages ("Tiny Hackable CUDA Language Model
+// Implementation", section 1; shared K/V heads, "Show HN: NanoEuler", section 2) for the
+// last Tq positions of a Tk-long sequence, the step of generation with a cache (one token,
+// or the K tokens of multi-token speculative decoding, "Show HN: NanoEuler", section 2):
+// query row i sits at position Tk - Tq + i and attends to the keys s <= Tk - Tq + i.
+//
+// The work is HBM-bound (every key and value row of the cache is read once per K/V head, and
+// there are few queries to reuse it), so the design is about bytes in flight, not matrix
+// cores:
+//  * Rows.  The g query heads sharing a K/V head and the Tq tokens form R = g * Tq rows,
+//    row r = i * g + hs; each wave takes a block of 32 rows as the 32 columns of its MFMA
+//    tiles (S^T = K Q^T, O^T += V^T P^T, as in attn_fwd), so one read of a key row serves
+//    every head of the group and every new token.
+//  * Split over the cache (split-K): each wave streams its own chunk of keys, 32 at a time;
+//    K rows go straight from HBM into the operand registers (the "split" layout is 16-byte
+//    runs of a key row), V rows through a wave-private LDS tile for the transposing read of
+//    V^T.  The next tile's loads are issued before the current tile is computed.  No
+//    barriers: each wave is independent.
+//  * Each chunk leaves a partial (O_c, LSE_c) in the workspace; a second kernel merges the
+//    chunks exactly, LSE = log sum_c e^{LSE_c}, O = sum_c e^{LSE_c - LSE} O_c (or the first
+//    kernel writes O and LSE directly when there is one chunk).
+#include <cmath>
+#include <type_traits>
+
+#include "ea_common.h"
+#include "ea_kernels.h"
+
+namespace ea {
+namespace {
+
+constexpr int kKT = 32;          // keys per tile
+constexpr int kWavesPerWG = 4;
+
+struct DecArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* part_o;    // [items][32 rows][D] fp32 (items = B * Hkv * nrb * nsplit)
+    float* part_lse;  // [items][32 rows] natural log, -inf for a row with no key in the chunk
+    int B, Tq, Tk, Hq, Hkv, g, R, nrb, nsplit, chunk;
+    float sl2;  // scale * log2(e)
+};
+
+template <typename T, int D>
+struct DecCfg {
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int NS = D / (2 * KPL);  // MFMA steps over head_dim
+    static constexpr int NDB = D / 32;
+    static constexpr int PS = 16 / KPL;       // MFMA steps over the 32 keys of a tile
+    static constexpr int EPC = 16 / sizeof(T);
+    static constexpr int CPR = D / EPC;       // 16-byte chunks per row
+    static constexpr int VS = D + EPC;        // V tile row stride in LDS (16 bytes of padding)
+    static constexpr int VCH = kKT * CPR / 64;  // V chunks per lane per tile
+    static constexpr int KCH = (D / 2) / EPC;   // K chunks per lane per tile
+    static_assert(kKT * CPR % 64 == 0, "V tile staging");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArgs a) {
+    using C = DecCfg<T, D>;
+    using M = Mfma<T>;
+    using frag = typename M::frag;
+    constexpr int KPL = C::KPL;
+
+    __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * kKT * C::VS];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const long long item = (long long)blockIdx.x * kWavesPerWG + w;
+    const long long nitems = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
+    if (item >= nitems) return;
+    const int sp = (int)(item % a.nsplit);
+    long long rest = item / a.nsplit;
+    const int rb = (int)(rest % a.nrb);
+    rest /= a.nrb;
+    const int kvh = (int)(rest % a.Hkv);
+    const int b = (int)(rest / a.Hkv);
+    T* Vs = Vsh + w * kKT * C::VS;
+
+    const T* __restrict__ qp = static_cast<const T*>(a.q);
+    const T* __restrict__ kp = static_cast<const T*>(a.k);
+    const T* __restrict__ vp = static_cast<const T*>(a.v);
+    const int off = a.Tk - a.Tq;
+
+    // This lane's row (MFMA column): token i, head hs of the group; -1 keys for padding rows.
+    const int r = rb * 32 + l32;
+    const bool row_ok = r < a.R;
+    const int ti = row_ok ? r / a.g : 0;
+    const int hs = row_ok ? r % a.g : 0;
+    const int head = kvh * a.g + hs;
+    const int lastkey = row_ok ? off + ti : -1;
+    // Keys of this chunk that any row of the block sees.
+    const int rlast = min(a.R, rb * 32 + 32) - 1;
+    const int kend_block = off + rlast / a.g + 1;
+    const int k0 = sp * a.chunk;
+    const int k1 = min(k0 + a.chunk, kend_block);
+    const int ntiles = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
+
+    frag qf[C::NS];
+    if (row_ok) {
+        const T* row = qp + (((long long)b * a.Tq + ti) * a.Hq + head) * D + half * (D / 2);
+#pragma unroll
+        for (int c = 0; c < (D / 2) / C::EPC; ++c) {
+            const Vec16<T> v = ld16(row + c * C::EPC);
+#pragma unroll
+            for (int e = 0; e < C::EPC / KPL; ++e) qf[c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&v.raw)[e];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) qf[s] = frag{};
+    }
+
+    // Tile loads: K rows straight into the split operand (lane = key l32, half of head_dim),
+    // V rows as 16-byte chunks for the LDS tile.  Rows past the chunk read as zero.
+    Vec16<T> kreg[C::KCH], vreg[C::VCH];
+    const long long kv_row0 = (long long)b * a.Tk;
+    auto fetch = [&](int t) {
+        const int s = k0 + t * kKT + l32;
+        const bool ok = s < k1;
+        const T* krow = kp + ((kv_row0 + s) * a.Hkv + kvh) * D + half * (D / 2);
+#pragma unroll
+        for (int c = 0; c < C::KCH; ++c) kreg[c] = ok ? ld16(krow + c * C::EPC) : zero16<T>();
+#pragma unroll
+        for (int n = 0; n < C::VCH; ++n) {
+            const int u = lane + 64 * n;
+            const int key = u / C::CPR, part = u % C::CPR;
+            const int sv = k0 + t * kKT + key;
+            vreg[n] = (sv < k1) ? ld16(vp + ((kv_row0 + sv) * a.Hkv + kvh) * D + part * C::EPC) : zero16<T>();
+        }
+    };
+    auto wave_sync = [&]() {  // LDS writes of this wave visible to its later reads, and back
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    float mrun = -INFINITY, l = 0.0f;
+    f32x16 oacc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[db] = zero_acc();
+
+    if (ntiles > 0) fetch(0);
+    for (int t = 0; t < ntiles; ++t) {
+        // Commit V of tile t to LDS; take K of tile t from the registers.
+        wave_sync();  // the previous tile's V reads are done
+#pragma unroll
+        for (int n = 0; n < C::VCH; ++n) {
+            const int u = lane + 64 * n;
+            st16(&Vs[(u / C::CPR) * C::VS + (u % C::CPR) * C::EPC], vreg[n]);
+        }
+        frag kf[C::NS];
+#pragma unroll
+        for (int c = 0; c < C::KCH; ++c)
+#pragma unroll
+            for (int e = 0; e < C::EPC / KPL; ++e) kf[c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&kreg[c].raw)[e];
+        wave_sync();
+        if (t + 1 < ntiles) fetch(t + 1);
+
+        // S^T = K Q^T (lanes = rows, registers = keys), masked where key > the row's last key.
+        f32x16 sacc = zero_acc();
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) sacc = M::mma(kf[s], qf[s], sacc);
+        const int kbase = k0 + t * kKT;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            if (kbase + acc_row(rr, half) > lastkey) sacc[rr] = -INFINITY;
+            mx = fmaxf(mx, sacc[rr]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.sl2;
+        const float mnew = fmaxf(mrun, mx);
+        const float mbase = (mnew == -INFINITY) ? 0.0f : mnew;  // rows with no key so far
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mbase);
+        float rs = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(sacc[rr] * a.sl2 - mbase);
+            sacc[rr] = p;
+            rs += p;
+        }
+        l = l * alpha + rs;
+        mrun = mnew;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int ps = 0; ps < C::PS; ++ps) {
+            const frag pf = acc_to_frag<T>(sacc, ps * KPL);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+                oacc[db] = M::mma(load_rows_frag<T>(Vs, C::VS, 0, ps, db * 32), pf, oacc[db]);
+        }
+    }
+
+    // Row totals (the two lane halves hold different keys) and the chunk's result.
+    const float lt = l + __shfl_xor(l, 32, 64);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float lse = lt > 0.0f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
+    if (a.nsplit == 1) {
+        if (!row_ok) return;
+        T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) orow[db * 32 + acc_row(rr, half)] = from_f32<T>(oacc[db][rr] * inv);
+        if (half == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = lse;
+        return;
+    }
+    if (!row_ok) return;  // the merge reads real rows only
+    float* po = a.part_o + item * 32 * D + (long long)l32 * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) po[db * 32 + acc_row(rr, half)] = oacc[db][rr] * inv;
+    if (half == 0) a.part_lse[item * 32 + l32] = lse;
+}
+
+// Merge of the chunks: one thread per (row, 4 columns).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
+    constexpr int TPR = D / 4;  // threads per row
+    const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long nrows = (long long)a.B * a.Hkv * a.R;
+    if (u >= nrows * TPR) return;
+    const int c4 = (int)(u % TPR);
+    const long long row = u / TPR;
+    const int r = (int)(row % a.R);
+    const long long bk = row / a.R;  // b * Hkv + kvh
+    const int kvh = (int)(bk % a.Hkv);
+    const int b = (int)(bk / a.Hkv);
+    const int rb = r / 32, rl = r % 32;
+    const long long item0 = (bk * a.nrb + rb) * a.nsplit;
+    float m = -INFINITY;
+    for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_lse[(item0 + sp) * 32 + rl]);
+    float z = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+        const float ls = a.part_lse[(item0 + sp) * 32 + rl];
+        const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
+        z += wgt;
+        const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + ((item0 + sp) * 32 + rl) * D + c4 * 4);
+        acc += wgt * po;
+    }
+    const float inv = 1.0f / z;  // every row sees key 0, so some chunk has weight 1
+    const int ti = r / a.g, head = kvh * a.g + r % a.g;
+    T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D + c4 * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = from_f32<T>(acc[e] * inv);
+    if (c4 == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
+}
+
+// Chunking: enough independent waves to keep HBM busy (about 8 per CU), chunks of whole
+// 32-key tiles, at least two tiles each.
+struct DecPlan {
+    int nrb, nsplit, chunk;
+};
+
+DecPlan plan_decode(int B, int Tq, int Tk, int Hq, int Hkv) {
+    const int g = Hq / Hkv;
+    DecPlan p;
+    p.nrb = (g * Tq + 31) / 32;
+    const long long base = (long long)B * Hkv * p.nrb;
+    const long long target = 2048;
+    const int tiles = (Tk + kKT - 1) / kKT;
+    long long ns = (target + base - 1) / base;
+    ns = std::min<long long>(ns, std::max(1, tiles / 2));
+    ns = std::max<long long>(ns, 1);
+    const int tiles_per = (int)((tiles + ns - 1) / ns);
+    p.chunk = tiles_per * kKT;
+    p.nsplit = (Tk + p.chunk - 1) / p.chunk;
+    return p;
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
+    const long long items = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
+    const long long blocks = (items + kWavesPerWG - 1) / kWavesPerWG;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3((unsigned)blocks), dim3(64 * kWavesPerWG), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const long long threads = (long long)a.B * a.Hkv * a.R * (D / 4);
+    const long long mblocks = (threads + 255) / 256;
+    if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)mblocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Tq, int Tk, int Hq, int Hkv, int D) {
+    const DecPlan p = plan_decode(B, Tq, Tk, Hq, Hkv);
+    if (p.nsplit == 1) return 256;
+    const size_t items = (size_t)B * Hkv * p.nrb * p.nsplit;
+    const size_t ob = (items * 32 * D * sizeof(float) + 255) & ~(size_t)255;
+    const size_t lb = (items * 32 * sizeof(float) + 255) & ~(size_t)255;
+    return ob + lb;
+}
+
+hipError_t launch_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, int B, int Tq, int Tk, int Hq, int Hkv, int D,
+                              float scale, IoType dt, hipStream_t stream) {
+    const DecPlan p = plan_decode(B, Tq, Tk, Hq, Hkv);
+    DecArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    const size_t items = (size_t)B * Hkv * p.nrb * p.nsplit;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          ((items * 32 * D * sizeof(float) + 255) & ~(size_t)255));
+    a.B = B;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.g = Hq / Hkv;
+    a.R = a.g * Tq;
+    a.nrb = p.nrb;
+    a.nsplit = p.nsplit;
+    a.chunk = p.chunk;
+    a.sl2 = scale * kLog2e;
+    if (dt == kF32) {
+        if (D == 32) return launch_decode_t<float, 32>(a, stream);
+        if (D == 64) return launch_decode_t<float, 64>(a, stream);
+        return launch_decode_t<float, 128>(a, stream);
+    }
+    if (D == 32) return launch_decode_t<bf16, 32>(a, stream);
+    if (D == 64) return launch_decode_t<bf16, 64>(a, stream);
+    return launch_decode_t<bf16, 128>(a, stream);
+}
+
+}  // namespace ea

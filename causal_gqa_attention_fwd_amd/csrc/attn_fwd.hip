@@ -373,7 +373,8 @@ hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream)
 // Heads per workgroup: the largest divisor G of g that is at most four.
 // * head_dim <= 64, bf16, few query blocks (B * Hq * T / 32 <= 2048, i.e. fewer than two
 //   waves per SIMD): one 32-row block per head (two for G <= 2) and two key splits.
-// * head_dim <= 64 otherwise: two waves per head (four when G <= 2), no key split.
+// * head_dim <= 64 otherwise: two waves per head (four when G <= 2), no key split; for bf16
+//   head_dim 64 each wave then owns 64 query rows (QB = 2) if 512+ workgroups remain.
 // * head_dim 128: one wave per head (4/G when G <= 2), no key split (LDS and registers).
 // Every shape gives 4, 6 or 8 waves (3 or 4 for head_dim 128).
 template <typename T, int D>
@@ -415,6 +416,18 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
                 if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6, 2>(a, G, WPH, stream);
                 if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4, 2>(a, G, WPH, stream);
                 return launch_fwd_cfg<T, D, QB, BN, 8, 2>(a, G, WPH, stream);
+            }
+        }
+        // Without a key split, bf16 head_dim-64 waves own two 32-row query blocks (QB = 2)
+        // when that still leaves at least two workgroups per CU: every K / V fragment read
+        // from LDS then feeds two matrix-core instructions.
+        if constexpr (sizeof(T) == 2 && D == 64) {
+            const long long wgs = (long long)a.B * a.Hkv * ((a.Hq / a.Hkv) / G) *
+                                  ((a.T + WPH * 64 - 1) / (WPH * 64));
+            if (wgs >= 512) {
+                if (nw == 6) return launch_fwd_cfg<T, D, 2, BN, 6, 1>(a, G, WPH, stream);
+                if (nw == 4) return launch_fwd_cfg<T, D, 2, BN, 4, 1>(a, G, WPH, stream);
+                return launch_fwd_cfg<T, D, 2, BN, 8, 1>(a, G, WPH, stream);
             }
         }
         if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6, 1>(a, G, WPH, stream);

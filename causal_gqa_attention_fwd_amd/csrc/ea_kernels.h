@@ -57,4 +57,12 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
                            IoType dt, const RopeArgs* rope, hipStream_t stream);
 
+// Attention of Tq new query rows (q, o [B, Tq, Hq, D]; lse [B, Hq, Tq]) against a cache
+// k, v [B, Tk, Hkv, D], Tq <= Tk: query row i sits at position Tk - Tq + i.  The workspace
+// holds the per-chunk partials (decode_workspace_bytes, 256-byte aligned).
+size_t decode_workspace_bytes(int B, int Tq, int Tk, int Hq, int Hkv, int D);
+hipError_t launch_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, int B, int Tq, int Tk, int Hq, int Hkv, int D,
+                              float scale, IoType dt, hipStream_t stream);
+
 }  // namespace ea

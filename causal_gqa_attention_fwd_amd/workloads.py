@@ -132,3 +132,52 @@ def make_random(shape, seed: int, dtype: str = "f32", scale: float = 1.0) -> tor
     if scale != 1.0:
         a *= np.float32(scale)
     return torch.from_numpy(a).to(torch_dtype(dtype))
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One generation step against a KV cache: Tq new query rows per sequence and a cache
+    of Tk positions (those rows included)."""
+    name: str
+    B: int
+    Tq: int
+    Tk: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    seed: int
+
+    def hbm_bytes(self) -> int:
+        """Algorithmic bytes of one call: read q and the K/V cache, write o and lse."""
+        es = 4 if self.dtype == "f32" else 2
+        return (2 * self.B * self.Tq * self.Hq * self.D * es + 2 * self.B * self.Tk * self.Hkv * self.D * es
+                + self.B * self.Hq * self.Tq * 4)
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "batch": self.B, "new_tokens": self.Tq, "cache_len": self.Tk,
+                "q_heads": self.Hq, "kv_heads": self.Hkv, "head_dim": self.D, "io_dtype": self.dtype,
+                "seed": self.seed}
+
+
+DECODE_WORKLOADS = {
+    # One new token per sequence against an 8192-position cache, 32 Q / 8 KV heads, head_dim 128
+    # (the scaled GQA shape above, generating).
+    "decode_b8_tk8192": DecodeWorkload("decode_b8_tk8192", 8, 1, 8192, 32, 8, 128, "bf16", 1006),
+    # Four new tokens (multi-token speculative decoding) for the 12 Q / 4 KV GPU model.
+    "decode_mtp4_b16_tk1024": DecodeWorkload("decode_mtp4_b16_tk1024", 16, 4, 1024, 12, 4, 64, "bf16", 1007),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload | str) -> dict:
+    """Seeded N(0,1) q [B,Tq,Hq,D] and cache k, v [B,Tk,Hkv,D] (drawn in that order) as CPU
+    torch tensors of the workload's dtype."""
+    if isinstance(w, str):
+        w = DECODE_WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal((w.B, w.Tq, w.Hq, w.D), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Tk, w.Hkv, w.D), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Tk, w.Hkv, w.D), dtype=np.float32)
+    tdt = torch_dtype(w.dtype)
+    return {"q": torch.from_numpy(q).to(tdt), "k": torch.from_numpy(k).to(tdt), "v": torch.from_numpy(v).to(tdt)}
+

@@ -92,6 +92,28 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * attn_decode -- attention of Tq new query rows against a KV cache, the step of generation
+ * with a cache (one token at a time, or the K tokens of the multi-token prediction heads'
+ * speculative decoding: "Show HN: NanoEuler", section 2).  q [B, Tq, Hq, D] holds the
+ * queries of the last Tq positions of a Tk-long sequence; k, v [B, Tk, Hkv, D] hold the
+ * whole cache, those positions included.  Query row i sits at position Tk - Tq + i and
+ * attends causally to the keys s <= Tk - Tq + i:  O_i = softmax_s(scale * <q_i, k_s>) V,
+ * LSE_i = log sum_s exp(scale * <q_i, k_s>), with the same K/V-head map as attn_fwd.  With
+ * Tq = Tk the result is attn_fwd's (attn_fwd is the faster kernel for that case).
+ * Outputs: o [B, Tq, Hq, D] in dt; lse [B, Hq, Tq] float32 (natural log).
+ * The cache is split into chunks read by independent waves; workspace (at least
+ * attn_decode_workspace_size(...) bytes, 256-byte aligned, contents ignored) holds the
+ * per-chunk partial results, merged exactly by a second launch.
+ * Errors: as attn_fwd (with T = Tk), plus Tq < 1 or Tq > Tk (EA_ERR_INVALID_ARG), workspace
+ * too small (EA_ERR_WORKSPACE) or not 256-byte aligned (EA_ERR_ALIGN), and o, lse or the
+ * workspace overlapping an input or each other (EA_ERR_ALIAS).
+ */
+size_t attn_decode_workspace_size(int B, int Tq, int Tk, int Hq, int Hkv, int D, ea_dtype dt);
+ea_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int Tq, int Tk, int Hq,
+                      int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream);
+
+/*
  * attn_bwd_workspace_size -- bytes of device scratch attn_bwd needs: the per-row
  * D_t = sum_d dO * O as float32 [B, Hq, T], rounded up to 256 bytes.  Linear in T (never
  * T^2).  Returns 0 for invalid sizes.

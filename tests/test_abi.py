@@ -216,6 +216,33 @@ def test_bwd_rope_validation(L):
     assert mn(dq=fake(8)) == ALIAS
 
 
+def test_decode_workspace_and_validation(L):
+    ws = L.attn_decode_workspace_size(8, 1, 8192, 32, 8, 128, BF16)
+    assert ws >= 256 and ws % 256 == 0
+    assert L.attn_decode_workspace_size(1, 2, 1, 4, 2, 64, BF16) == 0      # Tq > Tk
+    assert L.attn_decode_workspace_size(1, 1, 10, 3, 2, 64, BF16) == 0     # Hq % Hkv
+    assert L.attn_decode_workspace_size(1, 1, 10, 4, 2, 48, BF16) == 0     # head_dim
+
+    def dec(q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), w=fake(5), wb=None, Tq=1, Tk=64,
+            D=64, scale=0.125):
+        if wb is None:
+            wb = max(256, L.attn_decode_workspace_size(2, Tq, Tk, 4, 2, 64, BF16))
+        return L.attn_decode(q, k, v, o, lse, w, wb, 2, Tq, Tk, 4, 2, D, scale, BF16, None)
+    assert dec(k=None) == NULL
+    assert dec(w=None) == NULL
+    for kw in (dict(Tq=0), dict(Tq=65), dict(Tk=0, Tq=1), dict(scale=0.0)):
+        assert dec(**kw) == INVALID, kw
+    assert dec(D=96) == UNSUP
+    assert dec(o=fake(3) + 8) == ALIGN
+    assert dec(w=fake(5) + 64) == ALIGN
+    big = L.attn_decode_workspace_size(2, 1, 4096, 4, 2, 64, BF16)
+    assert big > 256
+    assert dec(Tk=4096, wb=big - 1) == WS
+    assert dec(o=fake(0)) == ALIAS
+    assert dec(lse=fake(3) + 64) == ALIAS
+    assert dec(w=fake(1)) == ALIAS
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 4, 2, 64)
