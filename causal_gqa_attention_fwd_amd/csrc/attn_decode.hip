@@ -224,38 +224,55 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     if (half == 0) a.part_lse[item * 32 + l32] = lse;
 }
 
-// Merge of the chunks: one thread per (row, 4 columns).
+// Merge of the chunks: one wave per row.  The lanes first take the chunks' LSE values (max,
+// then weights e^{LSE_c - m} kept in LDS and their sum), then the columns of the row, each
+// lane summing its columns over the chunks in chunk order (deterministic).
+constexpr int kMaxSplit = 256;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
-    constexpr int TPR = D / 4;  // threads per row
-    const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long nrows = (long long)a.B * a.Hkv * a.R;
-    if (u >= nrows * TPR) return;
-    const int c4 = (int)(u % TPR);
-    const long long row = u / TPR;
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
+    constexpr int CPL = D >= 64 ? D / 64 : 1;  // columns per lane
+    __shared__ float wsh[kMaxSplit];
+    const int lane = threadIdx.x;
+    const long long row = blockIdx.x;  // (b * Hkv + kvh) * R + r
     const int r = (int)(row % a.R);
-    const long long bk = row / a.R;  // b * Hkv + kvh
+    const long long bk = row / a.R;
     const int kvh = (int)(bk % a.Hkv);
     const int b = (int)(bk / a.Hkv);
     const int rb = r / 32, rl = r % 32;
     const long long item0 = (bk * a.nrb + rb) * a.nsplit;
     float m = -INFINITY;
-    for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part_lse[(item0 + sp) * 32 + rl]);
+    for (int sp = lane; sp < a.nsplit; sp += 64) m = fmaxf(m, a.part_lse[(item0 + sp) * 32 + rl]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float z = 0.0f;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp = 0; sp < a.nsplit; ++sp) {
+    for (int sp = lane; sp < a.nsplit; sp += 64) {
         const float ls = a.part_lse[(item0 + sp) * 32 + rl];
         const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
+        wsh[sp] = wgt;
         z += wgt;
-        const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + ((item0 + sp) * 32 + rl) * D + c4 * 4);
-        acc += wgt * po;
     }
-    const float inv = 1.0f / z;  // every row sees key 0, so some chunk has weight 1
-    const int ti = r / a.g, head = kvh * a.g + r % a.g;
-    T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D + c4 * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[e] = from_f32<T>(acc[e] * inv);
-    if (c4 == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
+    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+    __syncthreads();
+    const int ti = r / a.g, head = kvh * a.g + r % a.g;
+    if (lane * CPL < D) {
+        float acc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+        const float* po = a.part_o + (item0 * 32 + rl) * D + lane * CPL;
+#pragma unroll 8
+        for (int sp = 0; sp < a.nsplit; ++sp) {
+            const float wgt = wsh[sp];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] += wgt * po[(long long)sp * 32 * D + c];
+        }
+        const float inv = 1.0f / z;  // every row sees key 0, so some chunk has weight 1
+        T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D + lane * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) orow[c] = from_f32<T>(acc[c] * inv);
+    }
+    if (lane == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
 }
 
 // Chunking: enough independent waves to keep HBM busy (about 8 per CU), chunks of whole
@@ -273,6 +290,7 @@ DecPlan plan_decode(int B, int Tq, int Tk, int Hq, int Hkv) {
     const int tiles = (Tk + kKT - 1) / kKT;
     long long ns = (target + base - 1) / base;
     ns = std::min<long long>(ns, std::max(1, tiles / 2));
+    ns = std::min<long long>(ns, kMaxSplit);
     ns = std::max<long long>(ns, 1);
     const int tiles_per = (int)((tiles + ns - 1) / ns);
     p.chunk = tiles_per * kKT;
@@ -289,10 +307,9 @@ hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const long long threads = (long long)a.B * a.Hkv * a.R * (D / 4);
-    const long long mblocks = (threads + 255) / 256;
-    if (mblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)mblocks), dim3(256), 0, stream, a);
+    const long long rows = (long long)a.B * a.Hkv * a.R;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)rows), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
