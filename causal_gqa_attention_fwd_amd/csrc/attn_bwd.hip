@@ -183,36 +183,44 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
     const int nq = a.ntq - i0;
     const int niter = g * nq;
 
-    // Staging of Q_i / dO_i (16-byte chunks, row-major), LSE and D: HBM -> registers -> LDS.
-    Vec16<T> qreg[C::NCH], dreg[C::NCH];
-    float lreg = 0.0f, treg = 0.0f;
-    auto fetch = [&](int it) {
+    // Staging of Q_i / dO_i (16-byte chunks, row-major), LSE and D: HBM -> registers -> LDS,
+    // through NSET register sets (two for bf16: each stage's loads then have two iterations to
+    // land; one for fp32, whose registers are already spent on wider fragments).
+    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    struct Stg {
+        Vec16<T> q[C::NCH], d[C::NCH];
+        float l, t;
+    };
+    Stg sa;
+    [[maybe_unused]] Stg sb;
+    auto fetch = [&](Stg& st, int it) {
+        Vec16<T>* qreg = st.q;
+        Vec16<T>* dreg = st.d;
         const int head = kvh * g + it / nq;
         const int i = i0 + it % nq;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
             const int c = tid + n * C::NT;
-            if (c < BM * C::CPR) {
+            if (BM * C::CPR % C::NT == 0 || c < BM * C::CPR) {
                 const int row = c / C::CPR, part = c % C::CPR;
-                const int t = i * BM + row;
-                if (t < a.T) {
-                    const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC;
-                    qreg[n] = ld16(qp + off);
-                    dreg[n] = ld16(dop + off);
-                } else {
-                    qreg[n] = zero16<T>();
-                    dreg[n] = zero16<T>();
-                }
+                // Rows past the end load a real row instead: their P is 0 (LSE = +inf below),
+                // so they contribute nothing, and the loads need no branch.
+                const int t = min(i * BM + row, a.T - 1);
+                const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC;
+                qreg[n] = ld16(qp + off);
+                dreg[n] = ld16(dop + off);
             }
         }
         if (tid < BM) {
             const int t = i * BM + tid;
             const long long ro = ((long long)b * a.Hq + head) * a.T;
-            lreg = (t < a.T) ? a.lse[ro + t] * kLog2e : INFINITY;
-            treg = (t < a.T) ? a.dt[ro + t] : 0.0f;
+            st.l = (t < a.T) ? a.lse[ro + t] * kLog2e : INFINITY;
+            st.t = (t < a.T) ? a.dt[ro + t] : 0.0f;
         }
     };
-    auto commit = [&](int stage) {
+    auto commit = [&](const Stg& st, int stage) {
+        const Vec16<T>* qreg = st.q;
+        const Vec16<T>* dreg = st.d;
         char* base = smem + stage * C::STAGE;
         T* Qs = reinterpret_cast<T*>(base + C::OFF_Q);
         T* dOs = reinterpret_cast<T*>(base + C::OFF_DO);
@@ -226,8 +234,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
             }
         }
         if (tid < BM) {
-            reinterpret_cast<float*>(base + C::OFF_LSE)[tid] = lreg;
-            reinterpret_cast<float*>(base + C::OFF_DT)[tid] = treg;
+            reinterpret_cast<float*>(base + C::OFF_LSE)[tid] = st.l;
+            reinterpret_cast<float*>(base + C::OFF_DT)[tid] = st.t;
         }
     };
 
@@ -277,25 +285,40 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         }
     };
 
+    // Stage s sits in register set s % NSET until it is committed, at the start of iteration
+    // s - 1; the set is then refilled with stage s + NSET.
     if (niter > 0) {
-        fetch(0);
-        commit(0);
-        if (niter > 1) fetch(1);
+        fetch(sa, 0);
+        commit(sa, 0);
+        if constexpr (NSET == 2) {
+            if (niter > 1) fetch(sb, 1);
+            if (niter > 2) fetch(sa, 2);
+        } else {
+            if (niter > 1) fetch(sa, 1);
+        }
     }
-    for (int it = 0; it < niter; ++it) {
+    auto iteration = [&](int it, Stg& nxt) {
         __syncthreads();  // stage it&1 visible; stage (it+1)&1 free
         if (it + 1 < niter) {
-            commit((it + 1) & 1);
-            if (it + 2 < niter) fetch(it + 2);
+            commit(nxt, (it + 1) & 1);
+            if (it + 1 + NSET < niter) fetch(nxt, it + 1 + NSET);
         }
         const int i = i0 + it % nq;
         // Skip blocks whose keys all follow their queries; mask blocks crossing the diagonal.
         const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * 32;
-        if (kfirst > qfirst + 31) continue;
+        if (kfirst > qfirst + 31) return;
         if (kfirst + 31 > qfirst)
             compute(it, it & 1, std::true_type{});
         else
             compute(it, it & 1, std::false_type{});
+    };
+    if constexpr (NSET == 2) {
+        for (int it = 0; it < niter; it += 2) {
+            iteration(it, sb);
+            if (it + 1 < niter) iteration(it + 1, sa);
+        }
+    } else {
+        for (int it = 0; it < niter; ++it) iteration(it, sa);
     }
 
     // Sum the dK/dV partials of the query blocks in LDS, last block first, then store from
@@ -437,27 +460,34 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
         }
     }
 
-    // Staging of one K/V tile, row-major 16-byte chunks.
-    Vec16<T> kreg[C::NCH], vreg[C::NCH];
-    auto fetch = [&](int j) {
+    // Staging of one K/V tile, row-major 16-byte chunks, through NSET register sets (two for
+    // bf16, so that each tile's loads have two iterations to land).
+    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    struct Stg {
+        Vec16<T> k[C::NCH], v[C::NCH];
+    };
+    Stg sa;
+    [[maybe_unused]] Stg sb;
+    auto fetch = [&](Stg& st, int j) {
+        Vec16<T>* kreg = st.k;
+        Vec16<T>* vreg = st.v;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
             const int c = tid + n * C::NT;
             if (c < BN * C::CPR) {
                 const int key = c / C::CPR, part = c % C::CPR;
                 const int s = j * BN + key;
-                if (s < a.T) {
-                    const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
-                    kreg[n] = ld16(kp + off);
-                    vreg[n] = ld16(vp + off);
-                } else {
-                    kreg[n] = zero16<T>();
-                    vreg[n] = zero16<T>();
-                }
+                // Keys past the end load a real row instead: they only occur in diagonal
+                // tiles, where the mask zeroes them, and the loads need no branch.
+                const long long off = ((kv_row0 + min(s, a.T - 1)) * a.Hkv + kvh) * D + part * C::EPC;
+                kreg[n] = ld16(kp + off);
+                vreg[n] = ld16(vp + off);
             }
         }
     };
-    auto commit = [&](int stage) {
+    auto commit = [&](const Stg& st, int stage) {
+        const Vec16<T>* kreg = st.k;
+        const Vec16<T>* vreg = st.v;
         T* Ks = smem + stage * C::STAGE;
         T* Vs = Ks + C::KBUF;
 #pragma unroll
@@ -522,22 +552,37 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
         }
     };
 
-    fetch(0);
-    commit(0);
-    if (jmax >= 1) fetch(1);
+    // Tile s sits in register set s % NSET until it is committed at the start of iteration
+    // s - 1; the set is then refilled with tile s + NSET.
+    fetch(sa, 0);
+    commit(sa, 0);
+    if constexpr (NSET == 2) {
+        if (jmax >= 1) fetch(sb, 1);
+        if (jmax >= 2) fetch(sa, 2);
+    } else {
+        if (jmax >= 1) fetch(sa, 1);
+    }
     const int qlast = min(q0 + 32, a.T) - 1;
     const int jfirst_masked = q0 / BN;
-    for (int j = 0; j <= jmax; ++j) {
+    auto iteration = [&](int j, Stg& nxt) {
         __syncthreads();
         if (j + 1 <= jmax) {
-            commit((j + 1) & 1);
-            if (j + 2 <= jmax) fetch(j + 2);
+            commit(nxt, (j + 1) & 1);
+            if (j + 1 + NSET <= jmax) fetch(nxt, j + 1 + NSET);
         }
-        if (!active || j * BN > qlast) continue;
+        if (!active || j * BN > qlast) return;
         if (j >= jfirst_masked)
             compute(j, j & 1, std::true_type{});
         else
             compute(j, j & 1, std::false_type{});
+    };
+    if constexpr (NSET == 2) {
+        for (int j = 0; j <= jmax; j += 2) {
+            iteration(j, sb);
+            if (j + 1 <= jmax) iteration(j + 1, sa);
+        }
+    } else {
+        for (int j = 0; j <= jmax; ++j) iteration(j, sa);
     }
 
     if (!active || tq >= a.T) return;

@@ -141,9 +141,18 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     }
 
     // Staging of one step (KSPL consecutive K/V tiles): HBM -> registers (fetch) -> LDS
-    // (commit), 16-byte chunks, consecutive lanes on consecutive chunks of a row.
-    Vec16<T> kreg[C::NCH], vreg[C::NCH];
-    auto fetch = [&](int step) {
+    // (commit), 16-byte chunks, consecutive lanes on consecutive chunks of a row, through NSET
+    // register sets (two for bf16 with 32-row waves, so that each step's loads have two steps
+    // to land; 64-row waves have no registers to spare).
+    constexpr int NSET = (sizeof(T) == 2 && QB == 1) ? 2 : 1;
+    struct Stg {
+        Vec16<T> k[C::NCH], v[C::NCH];
+    };
+    Stg sa;
+    [[maybe_unused]] Stg sb;
+    auto fetch = [&](Stg& sg, int step) {
+        Vec16<T>* kreg = sg.k;
+        Vec16<T>* vreg = sg.v;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
             const int u = tid + n * C::NT;
@@ -152,18 +161,18 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                 const int key = c / C::CPR, part = c % C::CPR;
                 const int j = step * KSPL + sp;
                 const int s = j * BN + key;
-                if (j <= jmax && s < a.T) {
-                    const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + part * C::EPC;
-                    kreg[n] = ld16(kp + off);
-                    vreg[n] = ld16(vp + off);
-                } else {
-                    kreg[n] = zero16<T>();
-                    vreg[n] = zero16<T>();
-                }
+                // Keys past the end (or of a tile past jmax, never computed) load a real row
+                // instead: they only occur in the diagonal tile, where the mask removes them,
+                // and the loads need no branch.
+                const long long off = ((kv_row0 + min(s, a.T - 1)) * a.Hkv + kvh) * D + part * C::EPC;
+                kreg[n] = ld16(kp + off);
+                vreg[n] = ld16(vp + off);
             }
         }
     };
-    auto commit = [&](int buf) {
+    auto commit = [&](const Stg& sg, int buf) {
+        const Vec16<T>* kreg = sg.k;
+        const Vec16<T>* vreg = sg.v;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
             const int u = tid + n * C::NT;
@@ -265,23 +274,38 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     };
 
     const int nsteps = jmax / KSPL + 1;
-    fetch(0);
-    commit(0);
-    if (nsteps > 1) fetch(1);
+    // Step s sits in register set s % NSET until it is committed at the start of step s - 1;
+    // the set is then refilled with step s + NSET.
+    fetch(sa, 0);
+    commit(sa, 0);
+    if constexpr (NSET == 2) {
+        if (nsteps > 1) fetch(sb, 1);
+        if (nsteps > 2) fetch(sa, 2);
+    } else {
+        if (nsteps > 1) fetch(sa, 1);
+    }
     // The causal diagonal of this wave lies in tile q0 / BN; earlier tiles need no mask.
     const int jfirst_masked = q0 / BN;
-    for (int st = 0; st < nsteps; ++st) {
+    auto step = [&](int st, Stg& nxt) {
         __syncthreads();  // step st visible in buffer st&1; step st-1's buffer is free
         if (st + 1 < nsteps) {
-            commit((st + 1) & 1);
-            if (st + 2 < nsteps) fetch(st + 2);
+            commit(nxt, (st + 1) & 1);
+            if (st + 1 + NSET < nsteps) fetch(nxt, st + 1 + NSET);
         }
         const int j = st * KSPL + ks;
-        if (!active || j > jmax || j * BN > qlast) continue;
+        if (!active || j > jmax || j * BN > qlast) return;
         if (j >= jfirst_masked)
             compute(j, st & 1, std::true_type{});
         else
             compute(j, st & 1, std::false_type{});
+    };
+    if constexpr (NSET == 2) {
+        for (int st = 0; st < nsteps; st += 2) {
+            step(st, sb);
+            if (st + 1 < nsteps) step(st + 1, sa);
+        }
+    } else {
+        for (int st = 0; st < nsteps; ++st) step(st, sa);
     }
 
     if constexpr (KSPL == 2) {
