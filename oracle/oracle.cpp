@@ -255,4 +255,116 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     return 0;
 }
 
+// Non-causal GQA attention: every query row sees every key row (the per-head attention the
+// blog prints beside its tiled FlashAttention, "Tiled FlashAttention": rows of Q against all
+// rows of K and V).  Per (b, h, t), kv = h / g:
+//   S_ts = scale * sum_d Q[b,t,h,d] K[b,s,kv,d],  s = 0 .. T-1
+//   O_t = sum_s softmax_s(S_t.) V[b,s,kv,:],  LSE_t = log sum_s exp(S_ts)
+// Returns 0, or 1 when Hq is not a multiple of Hkv.
+int oracle_attn_fwd_nc(const double* q, const double* k, const double* v, double* o, double* lse,
+                       long B, long T, long Hq, long Hkv, long D, double scale) {
+    if (Hkv <= 0 || Hq % Hkv != 0) return 1;
+    const long g = Hq / Hkv;
+#pragma omp parallel
+    {
+        std::vector<double> srow(T > 0 ? T : 1);
+#pragma omp for collapse(3) schedule(dynamic, 8)
+        for (long b = 0; b < B; ++b) {
+            for (long h = 0; h < Hq; ++h) {
+                for (long t = 0; t < T; ++t) {
+                    const long kv = h / g;
+                    const double* qt = q + q_index(b, t, h, 0, T, Hq, D);
+                    double m = -INFINITY;
+                    for (long s = 0; s < T; ++s) {
+                        const double* ks = k + q_index(b, s, kv, 0, T, Hkv, D);
+                        double acc = 0.0;
+                        for (long d = 0; d < D; ++d) acc += qt[d] * ks[d];
+                        srow[s] = scale * acc;
+                        if (srow[s] > m) m = srow[s];
+                    }
+                    double z = 0.0;
+                    for (long s = 0; s < T; ++s) z += std::exp(srow[s] - m);
+                    double* ot = o + q_index(b, t, h, 0, T, Hq, D);
+                    for (long d = 0; d < D; ++d) ot[d] = 0.0;
+                    for (long s = 0; s < T; ++s) {
+                        const double p = std::exp(srow[s] - m) / z;
+                        const double* vs = v + q_index(b, s, kv, 0, T, Hkv, D);
+                        for (long d = 0; d < D; ++d) ot[d] += p * vs[d];
+                    }
+                    lse[(b * Hq + h) * T + t] = m + std::log(z);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+// Backward of the non-causal attention above, analytic from the full softmax of one (b, h):
+// dP = dO V^T, D_t = sum_s P_ts dP_ts, dS = P (dP - D), dQ = scale dS K,
+// dK = scale sum_{h in group} dS^T Q, dV = sum_{h in group} P^T dO (overwritten).
+int oracle_attn_bwd_nc(const double* q, const double* k, const double* v, const double* dout,
+                       double* dq, double* dk, double* dv, long B, long T, long Hq, long Hkv,
+                       long D, double scale) {
+    if (Hkv <= 0 || Hq % Hkv != 0) return 1;
+    const long g = Hq / Hkv;
+    std::memset(dk, 0, sizeof(double) * (size_t)(B * T * Hkv * D));
+    std::memset(dv, 0, sizeof(double) * (size_t)(B * T * Hkv * D));
+    std::vector<double> P((size_t)T * (size_t)T), dS((size_t)T * (size_t)T);
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < Hq; ++h) {
+            const long kv = h / g;
+#pragma omp parallel for schedule(dynamic, 8)
+            for (long t = 0; t < T; ++t) {
+                double* prow = P.data() + (size_t)t * T;
+                double* dsrow = dS.data() + (size_t)t * T;
+                const double* qt = q + q_index(b, t, h, 0, T, Hq, D);
+                const double* dot = dout + q_index(b, t, h, 0, T, Hq, D);
+                double m = -INFINITY;
+                for (long s = 0; s < T; ++s) {
+                    const double* ks = k + q_index(b, s, kv, 0, T, Hkv, D);
+                    double acc = 0.0;
+                    for (long d = 0; d < D; ++d) acc += qt[d] * ks[d];
+                    prow[s] = scale * acc;
+                    if (prow[s] > m) m = prow[s];
+                }
+                double z = 0.0;
+                for (long s = 0; s < T; ++s) z += std::exp(prow[s] - m);
+                for (long s = 0; s < T; ++s) prow[s] = std::exp(prow[s] - m) / z;
+                double delta = 0.0;
+                for (long s = 0; s < T; ++s) {
+                    const double* vs = v + q_index(b, s, kv, 0, T, Hkv, D);
+                    double acc = 0.0;
+                    for (long d = 0; d < D; ++d) acc += dot[d] * vs[d];
+                    dsrow[s] = acc;
+                    delta += prow[s] * acc;
+                }
+                for (long s = 0; s < T; ++s) dsrow[s] = prow[s] * (dsrow[s] - delta);
+                double* dqt = dq + q_index(b, t, h, 0, T, Hq, D);
+                for (long d = 0; d < D; ++d) dqt[d] = 0.0;
+                for (long s = 0; s < T; ++s) {
+                    const double* ks = k + q_index(b, s, kv, 0, T, Hkv, D);
+                    for (long d = 0; d < D; ++d) dqt[d] += dsrow[s] * ks[d];
+                }
+                for (long d = 0; d < D; ++d) dqt[d] *= scale;
+            }
+#pragma omp parallel for schedule(dynamic, 8)
+            for (long s = 0; s < T; ++s) {
+                double* dks = dk + q_index(b, s, kv, 0, T, Hkv, D);
+                double* dvs = dv + q_index(b, s, kv, 0, T, Hkv, D);
+                for (long t = 0; t < T; ++t) {
+                    const double ds = dS[(size_t)t * T + s];
+                    const double p = P[(size_t)t * T + s];
+                    const double* qt = q + q_index(b, t, h, 0, T, Hq, D);
+                    const double* dot = dout + q_index(b, t, h, 0, T, Hq, D);
+                    for (long d = 0; d < D; ++d) {
+                        dks[d] += scale * ds * qt[d];
+                        dvs[d] += p * dot[d];
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 }  // extern "C"

@@ -14,6 +14,8 @@ What each function computes, and the passage it follows, is stated at the C defi
  * ``attn_bwd``  -- the analytic gradients of L = sum(dO * O) with respect to the post-RoPE
                     Q, K and V, dK/dV summed over each query-head group.
  * ``grads_raw`` -- the end-to-end gradients with respect to the pre-RoPE Q and K.
+ * ``attn_fwd_nc``, ``attn_bwd_nc`` -- the non-causal form (every query row sees every key
+                    row), the per-head attention the blog prints ("Tiled FlashAttention").
  * ``attn_fwd_kv`` -- the same causal attention for Tq new query rows against a cache of
                     Tk >= Tq keys (generation with a KV cache: "Show HN: NanoEuler", section 2,
                     speculative decoding with the MTP heads, and the chat REPL of its key
@@ -64,6 +66,10 @@ def _load():
         lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
         lib.oracle_attn_fwd_kv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, L, ctypes.c_double]
         lib.oracle_attn_fwd_kv.restype = ctypes.c_int
+        lib.oracle_attn_fwd_nc.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
+        lib.oracle_attn_fwd_nc.restype = ctypes.c_int
+        lib.oracle_attn_bwd_nc.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
+        lib.oracle_attn_bwd_nc.restype = ctypes.c_int
         lib.oracle_attn_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -145,6 +151,39 @@ def attn_fwd_kv(q, k, v, scale: float | None = None):
     if rc != 0:
         raise ValueError("attn_fwd_kv: bad shapes")
     return o, lse
+
+
+def attn_fwd_nc(q, k, v, scale: float | None = None):
+    """Non-causal GQA attention forward -> (O [B,T,Hq,D], LSE [B,Hq,T]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hq, Hkv, D = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, T), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_nc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
+                                    float(scale))
+    if rc != 0:
+        raise ValueError("attn_fwd_nc: bad head counts")
+    return o, lse
+
+
+def attn_bwd_nc(q, k, v, dout, scale: float | None = None):
+    """Gradients (dQ, dK, dV) of sum(dO * O) for the non-causal attention, float64."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, T, Hq, Hkv, D = _check_qkv(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().oracle_attn_bwd_nc(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    B, T, Hq, Hkv, D, float(scale))
+    if rc != 0:
+        raise ValueError("attn_bwd_nc: bad head counts")
+    return dq, dk, dv
 
 
 def attn_bwd(q, k, v, dout, scale: float | None = None):
