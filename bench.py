@@ -13,6 +13,11 @@ head_dim 64, bf16 I/O (the blog's benchmark shape).
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--extra NAMES]
+                    [--decode NAMES] [--noncausal NAMES]
+
+Besides the headline step, the line carries the other timed paths of the library: extra
+workloads of the same step ('extra'), attention against a KV cache ('decode') and the
+attention without the causal mask ('noncausal').
 """
 from __future__ import annotations
 
@@ -227,6 +232,67 @@ def time_decode(name, steps, warmup, torch, ea, W):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
+def time_noncausal(name, steps, warmup, torch, ea, W):
+    """attn_fwd_noncausal then attn_bwd_noncausal (its pre-pass and main launch) on the inputs
+    of a workload (no RoPE): TFLOP/s at 14 * D * B * Hq * T^2 (every query/key pair), with the
+    forward's and the backward's average durations from HIP events on the launch stream."""
+    w = W.WORKLOADS[name]
+    log("[bench] non-causal workload %s" % name)
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (inp[x].to(dev) for x in ("q_raw", "k_raw", "v", "dout"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    L = ea.lib()
+    dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+    nws = L.attn_bwd_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, dtc)
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    scale = 1.0 / (w.D ** 0.5)
+    p = lambda t: t.data_ptr()  # noqa: E731
+    fwd = (p(q), p(k), p(v), p(o), p(lse), w.B, w.T, w.Hq, w.Hkv, w.D, scale, dtc, stream)
+    bwd = (p(q), p(k), p(v), p(o), p(lse), p(do), p(dq), p(dk), p(dv), p(ws), nws, w.B, w.T, w.Hq,
+           w.Hkv, w.D, scale, dtc, stream)
+
+    def run(ev=None):
+        for i, (fn, a) in enumerate(((L.attn_fwd_noncausal, fwd), (L.attn_bwd_noncausal, bwd))):
+            if ev:
+                ev[i][0].record()
+            if fn(*a) != 0:
+                raise RuntimeError("non-causal attention failed")
+            if ev:
+                ev[i][1].record()
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    per = [[], []]
+    for _ in range(steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+        run(ev)
+        torch.cuda.synchronize()
+        for i in range(2):
+            per[i].append(ev[i][0].elapsed_time(ev[i][1]))
+    pairs = w.B * w.Hq * w.T * w.T
+    flops = 14 * w.D * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    fwd_us, bwd_us = (1000.0 * statistics.mean(x) for x in per)
+    return {"config": dict(w.describe(), causal=False), "steps": steps, "ms_per_step": round(ms, 4),
+            "value": round(tf, 3), "unit": "TFLOP/s", "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+            "flops_convention": "14*D*B*Hq*T^2",
+            "kernel_us": {"attn_fwd_noncausal": round(fwd_us, 2), "attn_bwd_noncausal": round(bwd_us, 2)},
+            "fwd_tflops": round(4 * w.D * pairs / (fwd_us * 1e-6) / 1e12, 2),
+            "bwd_tflops": round(10 * w.D * pairs / (bwd_us * 1e-6) / 1e12, 2)}
+
+
 def cpu_baseline(w, W):
     """The oracle (plain float64 C++, OpenMP) on the host cores: one whole step of the same
     workload (RoPE on Q and K, forward, analytic backward, inverse RoPE on dQ and dK)."""
@@ -270,6 +336,9 @@ def main() -> int:
     ap.add_argument("--decode", default="decode_b8_tk8192,decode_mtp4_b16_tk1024",
                     help="comma-separated decode workloads (attn_decode against a KV cache) reported "
                          "under 'decode'; empty to skip")
+    ap.add_argument("--noncausal", default="blog_t1024,long_t8192",
+                    help="comma-separated workloads run through attn_fwd_noncausal + attn_bwd_noncausal, "
+                         "reported under 'noncausal'; empty to skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -336,6 +405,8 @@ def main() -> int:
     out["extra"] = extra
     out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                      for name in [x for x in args.decode.split(",") if x]}
+    out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5), torch, ea, W)
+                        for name in [x for x in args.noncausal.split(",") if x]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on host cores")
         out["cpu_baseline"] = cpu_baseline(w, W)

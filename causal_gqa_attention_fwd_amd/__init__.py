@@ -12,6 +12,7 @@ built, or the tensors are not on a ROCm device, the calls raise.
     attn_bwd_rope(q, k, v, o, lse, dout, base=1e4, pos0=0, ...)
                          -> (dq, dk, dv) with dq, dk for the tensors before RoPE
     attn_decode(q, k_cache, v_cache, scale=None, ...)         -> (o, lse) for the last Tq rows
+    attn_fwd_noncausal / attn_bwd_noncausal                   -> as attn_fwd / attn_bwd, no mask
 
 Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
 dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
@@ -24,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_preprocess",
+__all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
            "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
@@ -52,10 +53,14 @@ def lib() -> ctypes.CDLL:
     L.rope_apply_qk.restype = ci
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_fwd.restype = ci
+    L.attn_fwd_noncausal.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_fwd_noncausal.restype = ci
     L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
     L.attn_bwd_workspace_size.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_bwd.restype = ci
+    L.attn_bwd_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_noncausal.restype = ci
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, vp]
     L.attn_bwd_preprocess.restype = ci
     L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -170,6 +175,16 @@ def _shapes(q, k, v):
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """Causal GQA attention forward; returns (o [B,T,Hq,D], lse [B,Hq,T] float32)."""
+    return _fwd("attn_fwd", q, k, v, scale, out, lse)
+
+
+def attn_fwd_noncausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """GQA attention forward without the causal mask (every query sees every key)."""
+    return _fwd("attn_fwd_noncausal", q, k, v, scale, out, lse)
+
+
+def _fwd(name, q, k, v, scale, out, lse):
     B, T, Hq, Hkv, D = _shapes(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -182,9 +197,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | N
     if tuple(l.shape) != (B, Hq, T):
         raise ValueError("lse must be [B, Hq, T]")
     with torch.cuda.device(q.device):
-        st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
-                            B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
-    _raise(st, "attn_fwd")
+        st = getattr(lib(), name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                                  B, T, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, name)
     return o, l
 
 
@@ -206,6 +221,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     return _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, None)
 
 
+def attn_bwd_noncausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                       lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
+                       workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
+                       dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Backward of attn_fwd_noncausal; returns (dq, dk, dv), dk/dv summed over each group."""
+    return _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, "noncausal")
+
+
 def attn_bwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                   lse: torch.Tensor, dout: torch.Tensor, base: float = 10000.0, pos0: int = 0,
                   scale: float | None = None, workspace: torch.Tensor | None = None,
@@ -217,6 +240,7 @@ def attn_bwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
 
 
 def _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, rope):
+    # rope: None (causal), "noncausal", or (base, pos0) for the fused RoPE backward.
     B, T, Hq, Hkv, D = _shapes(q, k, v)
     _check("o", o, 4, q.device, q.dtype)
     _check("dout", dout, 4, q.device, q.dtype)
@@ -232,7 +256,8 @@ def _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, rope):
         _check(name, t, 4, q.device, q.dtype)
         if t.shape != ref.shape:
             raise ValueError("%s has the wrong shape" % name)
-    wsfn = lib().attn_bwd_workspace_size if rope is None else lib().attn_bwd_rope_workspace_size
+    with_rope = isinstance(rope, tuple)
+    wsfn = lib().attn_bwd_rope_workspace_size if with_rope else lib().attn_bwd_workspace_size
     need = int(wsfn(B, T, Hq, Hkv, D, _dtype_code(q)))
     if workspace is None:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
@@ -242,12 +267,13 @@ def _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, rope):
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes, B, T, Hq, Hkv, D,
             float(scale), _dtype_code(q))
+    name = "attn_bwd_rope" if with_rope else ("attn_bwd" if rope is None else "attn_bwd_noncausal")
     with torch.cuda.device(q.device):
-        if rope is None:
-            st = lib().attn_bwd(*args, _stream(q.device))
-        else:
+        if with_rope:
             st = lib().attn_bwd_rope(*args, rope[0], rope[1], _stream(q.device))
-    _raise(st, "attn_bwd" if rope is None else "attn_bwd_rope")
+        else:
+            st = getattr(lib(), name)(*args, _stream(q.device))
+    _raise(st, name)
     return dq, dk, dv
 
 

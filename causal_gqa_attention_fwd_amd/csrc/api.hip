@@ -44,6 +44,28 @@ ea_status check_attn_sizes(int B, int T, int Hq, int Hkv, int D, float scale, in
     return EA_OK;
 }
 
+ea_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, bool causal,
+                   hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const Range rq = range(q, (size_t)B * T * Hq * D * es);
+    const Range rk = range(k, (size_t)B * T * Hkv * D * es);
+    const Range rv = range(v, (size_t)B * T * Hkv * D * es);
+    const Range ro = range(o, (size_t)B * T * Hq * D * es);
+    const Range rl = range(lse, (size_t)B * Hq * T * sizeof(float));
+    for (Range out : {ro, rl})
+        for (Range in : {rq, rk, rv})
+            if (overlap(out, in)) return EA_ERR_ALIAS;
+    if (overlap(ro, rl)) return EA_ERR_ALIAS;
+    return from_hip(ea::launch_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale,
+                                        static_cast<ea::IoType>(dt), causal, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,23 +121,13 @@ ea_status rope_apply_qk(const void* q, void* q_out, int Hq, const void* k, void*
 
 ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse) return EA_ERR_NULL;
-    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
-    if (st != EA_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return EA_ERR_ALIGN;
-    const size_t es = elem_size(dt);
-    const Range rq = range(q, (size_t)B * T * Hq * D * es);
-    const Range rk = range(k, (size_t)B * T * Hkv * D * es);
-    const Range rv = range(v, (size_t)B * T * Hkv * D * es);
-    const Range ro = range(o, (size_t)B * T * Hq * D * es);
-    const Range rl = range(lse, (size_t)B * Hq * T * sizeof(float));
-    for (Range out : {ro, rl})
-        for (Range in : {rq, rk, rv})
-            if (overlap(out, in)) return EA_ERR_ALIAS;
-    if (overlap(ro, rl)) return EA_ERR_ALIAS;
-    return from_hip(ea::launch_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale,
-                                        static_cast<ea::IoType>(dt), stream));
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, true, stream);
+}
+
+ea_status attn_fwd_noncausal(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                             hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, false, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int T, int Hq, int Hkv, int D, ea_dtype dt) {
@@ -201,7 +213,7 @@ ea_status check_alias(const Range (&ins)[NI], const Range (&outs)[NO]) {
 ea_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
-                   ea_dtype dt, const ea::RopeArgs* rope, hipStream_t stream) {
+                   ea_dtype dt, const ea::RopeArgs* rope, bool causal, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return EA_ERR_NULL;
     ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
     if (st != EA_OK) return st;
@@ -217,7 +229,8 @@ ea_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
     const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb), range(workspace, z.ws)};
     if ((st = check_alias(ins, outs)) != EA_OK) return st;
     return from_hip(ea::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, T, Hq,
-                                        Hkv, D, scale, static_cast<ea::IoType>(dt), rope, stream));
+                                        Hkv, D, scale, static_cast<ea::IoType>(dt), rope, causal,
+                                        stream));
 }
 
 ea_status pre_impl(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B,
@@ -255,7 +268,7 @@ ea_status main_impl(const void* q, const void* k, const void* v, const float* ls
     if ((st = check_alias(ins, outs)) != EA_OK) return st;
     return from_hip(ea::launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, const_cast<void*>(workspace),
                                         B, T, Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), rope,
-                                        stream));
+                                        true, stream));
 }
 
 }  // namespace
@@ -267,7 +280,15 @@ ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D, float scale,
                    ea_dtype dt, hipStream_t stream) {
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv,
-                    D, scale, dt, nullptr, stream);
+                    D, scale, dt, nullptr, true, stream);
+}
+
+ea_status attn_bwd_noncausal(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, int B, int T, int Hq,
+                             int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream) {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv,
+                    D, scale, dt, nullptr, false, stream);
 }
 
 ea_status attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
@@ -277,7 +298,7 @@ ea_status attn_bwd_rope(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream) {
     const ea::RopeArgs rope{base, pos0};
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv,
-                    D, scale, dt, &rope, stream);
+                    D, scale, dt, &rope, true, stream);
 }
 
 ea_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,

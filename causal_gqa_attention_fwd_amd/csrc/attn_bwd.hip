@@ -94,6 +94,7 @@ struct BwdArgs {
     int ntq;          // dK/dV role: query stages (BM rows each)
     int ntq_dq;       // dq role: query tiles (32 * WPH rows each)
     int roles;        // 1: dK/dV only, 2: dQ only, 3: both in one launch
+    int causal;       // 1: key s visible to query t iff s <= t; 0: every key visible
     float sl2;        // scale * log2(e)
     float scale;
     const float* rope_cs;  // (cos, sin) per (t, pair) for the inverse RoPE on dQ / dK, or null
@@ -178,8 +179,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         dvacc[db] = zero_acc();
     }
 
-    // Iterations: every head of the group x every query tile on or below the diagonal.
-    const int i0 = (j * BN) / BM;
+    // Iterations: every head of the group x every query tile on or below the diagonal (every
+    // query tile without the causal mask).
+    const int i0 = a.causal ? (j * BN) / BM : 0;
     const int nq = a.ntq - i0;
     const int niter = g * nq;
 
@@ -305,9 +307,11 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         }
         const int i = i0 + it % nq;
         // Skip blocks whose keys all follow their queries; mask blocks crossing the diagonal.
+        // Without the causal mask nothing is masked: keys past the end have K = V = 0 and
+        // their dK / dV are never stored; queries past the end have P = 0 (LSE = +inf).
         const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * 32;
-        if (kfirst > qfirst + 31) return;
-        if (kfirst + 31 > qfirst)
+        if (a.causal && kfirst > qfirst + 31) return;
+        if (a.causal && kfirst + 31 > qfirst)
             compute(it, it & 1, std::true_type{});
         else
             compute(it, it & 1, std::false_type{});
@@ -425,8 +429,9 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     const int q0 = tile * BM + sub * 32;
     const bool active = wave_used && q0 < a.T;
     const int wg_last = min(tile * BM + BM, a.T) - 1;
-    const int jmax = wg_last / BN;
+    const int jmax = (a.causal ? wg_last : a.T - 1) / BN;
     const int tq = q0 + l32;  // this lane's query
+    const int lim = a.causal ? tq : a.T - 1;  // last key it sees
 
     const T* __restrict__ qp = static_cast<const T*>(a.q);
     const T* __restrict__ kp = static_cast<const T*>(a.k);
@@ -532,7 +537,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
             for (int r = 0; r < 16; ++r) {
                 float p = __builtin_amdgcn_exp2f(sacc[kb][r] * a.sl2 - lse2);
                 if constexpr (MASK) {
-                    if (j * BN + kb * 32 + acc_row(r, half) > tq) p = 0.0f;
+                    if (j * BN + kb * 32 + acc_row(r, half) > lim) p = 0.0f;
                 }
                 pacc[kb][r] = p * (pacc[kb][r] - dtv);
             }
@@ -563,14 +568,15 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
         if (jmax >= 1) fetch(sa, 1);
     }
     const int qlast = min(q0 + 32, a.T) - 1;
-    const int jfirst_masked = q0 / BN;
+    // Causal: tiles from the diagonal's on are masked.  Otherwise only a ragged last tile.
+    const int jfirst_masked = a.causal ? q0 / BN : ((a.T % BN) ? (a.T - 1) / BN : INT_MAX);
     auto iteration = [&](int j, Stg& nxt) {
         __syncthreads();
         if (j + 1 <= jmax) {
             commit(nxt, (j + 1) & 1);
             if (j + 1 + NSET <= jmax) fetch(nxt, j + 1 + NSET);
         }
-        if (!active || j * BN > qlast) return;
+        if (!active || (a.causal && j * BN > qlast)) return;
         if (j >= jfirst_masked)
             compute(j, j & 1, std::true_type{});
         else
@@ -797,8 +803,9 @@ float* ws_rope(void* ws, int B, int T, int Hq) {
 
 BwdArgs make_args(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, void* workspace, int B, int T, int Hq, int Hkv,
-                  float scale, bool rope = false) {
+                  float scale, bool rope = false, bool causal = true) {
     BwdArgs a{};
+    a.causal = causal ? 1 : 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -855,19 +862,20 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
                            int T, int Hq, int Hkv, int D, float scale, IoType dt, bool rope,
-                           hipStream_t stream) {
-    const BwdArgs a = make_args(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, scale, rope);
+                           bool causal, hipStream_t stream) {
+    const BwdArgs a = make_args(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, scale, rope,
+                                causal);
     return dt == kF32 ? launch_bwd_roles<float>(a, D, 3, stream) : launch_bwd_roles<bf16>(a, D, 3, stream);
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
-                           IoType dt, const RopeArgs* rope, hipStream_t stream) {
+                           IoType dt, const RopeArgs* rope, bool causal, hipStream_t stream) {
     hipError_t e = launch_bwd_pre(o, dout, workspace, B, T, Hq, D, dt, rope, stream);
     if (e != hipSuccess) return e;
     return launch_bwd_main(q, k, v, lse, dout, dq, dk, dv, workspace, B, T, Hq, Hkv, D, scale, dt,
-                           rope != nullptr, stream);
+                           rope != nullptr, causal, stream);
 }
 
 }  // namespace ea

@@ -53,6 +53,7 @@ struct FwdArgs {
     int WPH;  // waves per head
     int nhc;  // head chunks per K/V head (g / G)
     int ntq;  // query tiles
+    int causal;  // 1: key s visible to query t iff s <= t; 0: every key visible
     float sl2;  // scale * log2(e)
 };
 
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     const bool active = q0 < a.T;
     const int qlast = min(q0 + C::QW, a.T) - 1;
     const int wg_last = min(tile * BM + BM, a.T) - 1;
-    const int jmax = wg_last / BN;
+    const int jmax = (a.causal ? wg_last : a.T - 1) / BN;
 
     const T* __restrict__ qp = static_cast<const T*>(a.q);
     const T* __restrict__ kp = static_cast<const T*>(a.k);
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                 const int j = step * KSPL + sp;
                 const int s = j * BN + key;
                 // Keys past the end (or of a tile past jmax, never computed) load a real row
-                // instead: they only occur in the diagonal tile, where the mask removes them,
-                // and the loads need no branch.
+                // instead: they only occur in a masked tile (the diagonal, or the ragged last
+                // tile without the causal mask), and the loads need no branch.
                 const long long off = ((kv_row0 + min(s, a.T - 1)) * a.Hkv + kvh) * D + part * C::EPC;
                 kreg[n] = ld16(kp + off);
                 vreg[n] = ld16(vp + off);
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int tq = q0 + qb * 32 + l32;
+            // Last key this lane's query sees.
+            const int lim = a.causal ? q0 + qb * 32 + l32 : a.T - 1;
             float mx = -INFINITY;
 #pragma unroll
             for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (MASK) {
                         const int key = j * BN + kb2 * 32 + acc_row(r, half);
-                        if (key > tq) sacc[qb][kb2][r] = -INFINITY;
+                        if (key > lim) sacc[qb][kb2][r] = -INFINITY;
                     }
                     mx = fmaxf(mx, sacc[qb][kb2][r]);
                 }
@@ -284,8 +286,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
     } else {
         if (nsteps > 1) fetch(sa, 1);
     }
-    // The causal diagonal of this wave lies in tile q0 / BN; earlier tiles need no mask.
-    const int jfirst_masked = q0 / BN;
+    // Causal: the diagonal of this wave lies in tile q0 / BN; earlier tiles need no mask.
+    // Otherwise only a ragged last tile (keys past the end) is masked.
+    const int jfirst_masked = a.causal ? q0 / BN : ((a.T % BN) ? (a.T - 1) / BN : INT_MAX);
     auto step = [&](int st, Stg& nxt) {
         __syncthreads();  // step st visible in buffer st&1; step st-1's buffer is free
         if (st + 1 < nsteps) {
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
             if (st + 1 + NSET < nsteps) fetch(nxt, st + 1 + NSET);
         }
         const int j = st * KSPL + ks;
-        if (!active || j > jmax || j * BN > qlast) return;
+        if (!active || j > jmax || (a.causal && j * BN > qlast)) return;
         if (j >= jfirst_masked)
             compute(j, st & 1, std::true_type{});
         else
@@ -464,8 +467,9 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
-                           hipStream_t stream) {
+                           bool causal, hipStream_t stream) {
     FwdArgs a{};
+    a.causal = causal ? 1 : 0;
     a.q = q;
     a.k = k;
     a.v = v;

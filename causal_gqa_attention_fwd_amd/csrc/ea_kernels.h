@@ -23,10 +23,11 @@ hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, vo
                             int B, int T, int D, IoType dt, double base, int pos0, int inverse,
                             hipStream_t stream);
 
-// Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log).
+// Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log); causal = false lets every query
+// see every key.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
-                           hipStream_t stream);
+                           bool causal, hipStream_t stream);
 
 // Workspace of the backward: D_t = sum_d dO * O as fp32 [B, Hq, T], 256-byte aligned; with
 // rope, then the (cos, sin) table of the inverse RoPE, fp32 [T, D/2, 2], 256-byte aligned.
@@ -45,17 +46,18 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          const void* dout, void* dq, void* workspace, int B, int T, int Hq,
                          int Hkv, int D, float scale, IoType dt, hipStream_t stream);
 // dkdv and dq in one launch (the two roles' workgroups interleaved, heaviest first); with
-// rope, dq and dk are rotated by -phi (table from pre) before they are stored.
+// rope, dq and dk are rotated by -phi (table from pre) before they are stored.  dkdv and dq
+// alone are causal; main and the full backward take the mask as an argument.
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
                            int T, int Hq, int Hkv, int D, float scale, IoType dt, bool rope,
-                           hipStream_t stream);
+                           bool causal, hipStream_t stream);
 
 // Backward: dq, dk, dv from q, k, v, o, lse, dout; workspace as above (rope may be null).
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            void* workspace, int B, int T, int Hq, int Hkv, int D, float scale,
-                           IoType dt, const RopeArgs* rope, hipStream_t stream);
+                           IoType dt, const RopeArgs* rope, bool causal, hipStream_t stream);
 
 // Attention of Tq new query rows (q, o [B, Tq, Hq, D]; lse [B, Hq, Tq]) against a cache
 // k, v [B, Tk, Hkv, D], Tq <= Tk: query row i sits at position Tk - Tq + i.  The workspace

@@ -92,6 +92,18 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * attn_fwd_noncausal -- attn_fwd without the causal mask: every query row sees every key row,
+ * S_ts = scale * <q_t, k_s> for all s in [0, T);  O_t = sum_s softmax_s(S_t.) v_s;
+ * LSE_t = log sum_s exp(S_ts).  This is the form of the tiled FlashAttention forward that the
+ * smartinfralog.com post on NanoEuler prints (section "Tiled FlashAttention": each query
+ * tile walks over every K/V tile).  Same arguments, layouts, K/V-head map and errors as
+ * attn_fwd; the lse it returns is the one attn_bwd_noncausal needs.
+ */
+ea_status attn_fwd_noncausal(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                             hipStream_t stream);
+
+/*
  * attn_decode -- attention of Tq new query rows against a KV cache, the step of generation
  * with a cache (one token at a time, or the K tokens of the multi-token prediction heads'
  * speculative decoding: "Show HN: NanoEuler", section 2).  q [B, Tq, Hq, D] holds the
@@ -136,6 +148,16 @@ ea_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv,
                    int D, float scale, ea_dtype dt, hipStream_t stream);
+
+/*
+ * attn_bwd_noncausal -- the backward of attn_fwd_noncausal (no mask: every key contributes
+ * to every query's gradient).  Inputs are that forward's q, k, v, o, lse and dout; outputs,
+ * workspace (attn_bwd_workspace_size bytes), determinism and errors as attn_bwd.
+ */
+ea_status attn_bwd_noncausal(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, int B, int T, int Hq,
+                             int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream);
 
 /*
  * The stages of attn_bwd, for callers that schedule them separately: attn_bwd is exactly

@@ -39,6 +39,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_rope",
+              "attn_fwd_noncausal", "attn_bwd_noncausal", "attn_decode",
               "attn_bwd_rope_workspace_size", "euler_attn_status_string", "euler_attn_version"):
         assert n in names
 
@@ -87,11 +88,14 @@ def test_rope_qk_validation(L):
 
 
 def fwd(L, q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), B=2, T=16, Hq=4, Hkv=2,
-        D=64, scale=0.125, dt=BF16):
-    return L.attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, None)
+        D=64, scale=0.125, dt=BF16, fn="attn_fwd"):
+    return getattr(L, fn)(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, None)
 
 
-def test_fwd_validation(L):
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_noncausal"])
+def test_fwd_validation(L, fn):
+    def fwd(L, **kw):
+        return globals()["fwd"](L, fn=fn, **kw)
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(L, **{name: None}) == NULL, name
     for kw in (dict(B=0), dict(T=0), dict(Hq=0), dict(Hkv=0), dict(Hq=3, Hkv=2),
@@ -123,13 +127,16 @@ def test_workspace_size(L):
 
 def bwd(L, q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), do=fake(5), dq=fake(6),
         dk=fake(7), dv=fake(8), ws=fake(9), wsb=None, B=2, T=16, Hq=4, Hkv=2, D=64, scale=0.125,
-        dt=BF16):
+        dt=BF16, fn="attn_bwd"):
     if wsb is None:
         wsb = L.attn_bwd_workspace_size(B, T, Hq, Hkv, D, dt)
-    return L.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, wsb, B, T, Hq, Hkv, D, scale, dt, None)
+    return getattr(L, fn)(q, k, v, o, lse, do, dq, dk, dv, ws, wsb, B, T, Hq, Hkv, D, scale, dt, None)
 
 
-def test_bwd_validation(L):
+@pytest.mark.parametrize("fn", ["attn_bwd", "attn_bwd_noncausal"])
+def test_bwd_validation(L, fn):
+    def bwd(L, **kw):
+        return globals()["bwd"](L, fn=fn, **kw)
     for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
         assert bwd(L, **{name: None}) == NULL, name
     for kw in (dict(B=0), dict(T=0), dict(Hq=6, Hkv=4), dict(scale=0.0)):
@@ -250,3 +257,5 @@ def test_binding_refuses_cpu_tensors():
         ea.rope_apply(x)
     with pytest.raises(RuntimeError):
         ea.attn_fwd(x, x[:, :, :1].contiguous(), x[:, :, :1].contiguous())
+    with pytest.raises(RuntimeError):
+        ea.attn_fwd_noncausal(x, x[:, :, :1].contiguous(), x[:, :, :1].contiguous())
