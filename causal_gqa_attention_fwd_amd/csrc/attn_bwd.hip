@@ -22,6 +22,7 @@
 // Splitting dQ out costs the S and dP products a second time (14D instead of 10D FLOPs per
 // query/key pair) but removes the fp32 atomic traffic of a fused kernel, which on this chip
 // costs more than the extra matrix-core work at these sizes.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -78,6 +79,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
     }
 }
 
+constexpr int kMaxOrder = 256;  // items per (batch, K/V head) the dispatch table can hold
+
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -98,6 +101,11 @@ struct BwdArgs {
     float sl2;        // scale * log2(e)
     float scale;
     const float* rope_cs;  // (cos, sin) per (t, pair) for the inverse RoPE on dQ / dK, or null
+    // Dispatch order of one (batch, K/V head)'s items when both roles share a launch (roles
+    // 3): entry m is dK/dV item e (e < 0x8000) or dQ item e - 0x8000.  norder = 0: use the
+    // proportional merge instead.
+    int norder;
+    unsigned short order[kMaxOrder];
 };
 
 // ---------------------------------------------------------------------------------------
@@ -635,9 +643,10 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
 // ---------------------------------------------------------------------------------------
 // One launch for both roles.  Items are numbered per (batch, K/V head): dK/dV items
 // j = 0 .. ntk-1 (key tile j, heaviest first) and dQ items i = 0 .. nqi-1 (heaviest first).
-// With both roles, the two lists are merged by relative position (j/ntk vs i/nqi), so the
-// heavy items of both roles are dispatched first and each role's light tail overlaps the
-// other's work.
+// With both roles, the items are dispatched in decreasing order of their estimated cost
+// (longest first, from a table the host sorts), so the longest items start first and the
+// short ones fill in behind them; when a (batch, K/V head) has more items than the table
+// holds, the two lists are merged by relative position (j/ntk vs i/nqi) instead.
 // ---------------------------------------------------------------------------------------
 struct Sched {
     int ntk, nqi;
@@ -677,6 +686,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
     } else if (a.roles == 2) {
         is_dkdv = false;
         item = m;
+    } else if (a.norder > 0) {
+        const int e = a.order[m];
+        is_dkdv = e < 0x8000;
+        item = is_dkdv ? e : e - 0x8000;
     } else {
         // Largest j with dkdv_rank(j) <= m (dkdv_rank is increasing, dkdv_rank(0) = 0).
         const Sched sc{a.ntk, nqi};
@@ -737,6 +750,35 @@ constexpr int dkdv_waves() {
     return (D >= 128 || (sizeof(T) == 4 && D == 64)) ? 4 : 8;
 }
 
+// Longest-first dispatch table of one (batch, K/V head)'s items for the shared launch.  Cost
+// of an item = its iterations x the MFMA work of one iteration (8 D FLOPs per pair for the
+// dK/dV role: S, dP, dV, dK; 6 D for the dQ role: S, dP, dQ).  Both roles' lists are already
+// in non-increasing cost order, so one merge sorts them; ties keep dK/dV items first.
+template <typename K>
+void fill_order(BwdArgs& a) {
+    const int nqi = a.ntq_dq * a.nhc;
+    if (a.ntk + nqi > kMaxOrder) return;
+    const int g = a.Hq / a.Hkv;
+    const int BN = K::Dk::BN, BMq = a.WPH * 32, BNq = K::BNQ;
+    auto cost_dkdv = [&](int j) {
+        const int stages = a.causal ? a.ntq - (j * BN) / K::BM : a.ntq;
+        return (long long)g * stages * (BN * K::BM * 8);
+    };
+    auto cost_dq = [&](int i) {
+        const int tile = a.ntq_dq - 1 - i / a.nhc;
+        const int last = a.causal ? std::min(tile * BMq + BMq, a.T) - 1 : a.T - 1;
+        return (long long)(last / BNq + 1) * (BMq * a.G * BNq * 6);
+    };
+    int j = 0, i = 0, n = 0;
+    while (j < a.ntk || i < nqi) {
+        if (i >= nqi || (j < a.ntk && cost_dkdv(j) >= cost_dq(i)))
+            a.order[n++] = (unsigned short)j++;
+        else
+            a.order[n++] = (unsigned short)(0x8000 + i++);
+    }
+    a.norder = n;
+}
+
 template <typename T, int D, int NW>
 hipError_t launch_bwd_cfg(const BwdArgs& a0, int G, int WPH, int roles, hipStream_t stream) {
     using K = BwdKernelCfg<T, D, NW>;
@@ -748,6 +790,8 @@ hipError_t launch_bwd_cfg(const BwdArgs& a0, int G, int WPH, int roles, hipStrea
     a.ntq = (a.T + K::BM - 1) / K::BM;
     a.ntq_dq = (a.T + WPH * 32 - 1) / (WPH * 32);
     a.roles = roles;
+    a.norder = 0;
+    if (roles == 3) fill_order<K>(a);
     long long items = 0;
     if (roles & 1) items += a.ntk;
     if (roles & 2) items += (long long)a.ntq_dq * a.nhc;
