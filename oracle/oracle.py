@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` may import this module; the product path (the HIP library and its Python
 binding) never does.  The arithmetic lives in ``oracle.cpp`` (C++, float64, OpenMP), built
-here with g++; this module only marshals numpy arrays.  It shares no code with the HIP path.
+here with g++; this module only marshals numpy arrays (the projections are numpy float64
+matrix products, written here).  It shares no code with the HIP path.
 
 What each function computes, and the passage it follows, is stated at the C definition:
  * ``rope``      -- rotary embedding on queries and keys ("Show HN: NanoEuler", section 2;
@@ -16,6 +17,11 @@ What each function computes, and the passage it follows, is stated at the C defi
  * ``grads_raw`` -- the end-to-end gradients with respect to the pre-RoPE Q and K.
  * ``attn_fwd_nc``, ``attn_bwd_nc`` -- the non-causal form (every query row sees every key
                     row), the per-head attention the blog prints ("Tiled FlashAttention").
+ * ``gemm``, ``qkv_proj``, ``qkv_proj_bwd`` -- the projections on either side of the
+                    attention: matrix products in float64 (numpy's matmul as the library
+                    step), the QKV split into heads, RoPE (``rope`` above) on queries and keys
+                    ("Show HN: NanoEuler", sections 2 and 4; "Tiny Hackable ...", section 1:
+                    the attention result is projected back to the model dimension).
  * ``attn_fwd_kv`` -- the same causal attention for Tq new query rows against a cache of
                     Tk >= Tq keys (generation with a KV cache: "Show HN: NanoEuler", section 2,
                     speculative decoding with the MTP heads, and the chat REPL of its key
@@ -217,3 +223,51 @@ def grads_raw(q_raw, k_raw, v, dout, base: float = 10000.0, scale: float | None 
     qr, kr = rope(q_raw, base), rope(k_raw, base)
     dq, dk, dv = attn_bwd(qr, kr, v, dout, scale)
     return rope(dq, base, inverse=True), rope(dk, base, inverse=True), dv
+
+
+def gemm(a, b, trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+    """op(A) op(B) in float64; op transposes a stored operand when its flag is set."""
+    a, b = _f64(a), _f64(b)
+    if a.ndim != 2 or b.ndim != 2:
+        raise ValueError("gemm expects 2-D operands")
+    opa = a.T if trans_a else a
+    opb = b.T if trans_b else b
+    if opa.shape[1] != opb.shape[0]:
+        raise ValueError("inner dimensions differ")
+    return opa @ opb
+
+
+def _split_qkv(y, B, T, Hq, Hkv, D):
+    q = y[:, :Hq * D].reshape(B, T, Hq, D)
+    k = y[:, Hq * D:(Hq + Hkv) * D].reshape(B, T, Hkv, D)
+    v = y[:, (Hq + Hkv) * D:].reshape(B, T, Hkv, D)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def qkv_proj(x, w_qkv, Hq: int, Hkv: int, D: int, rope_on: bool = True, base: float = 10000.0,
+             pos0: int = 0):
+    """QKV projection of x [B, T, C] by w_qkv [C, (Hq + 2 Hkv) D] (columns: query heads, key
+    heads, value heads): q, k, v as [B, T, H, D]; with rope_on, q and k rotated by rope()."""
+    x, w = _f64(x), _f64(w_qkv)
+    B, T, C = x.shape
+    if w.shape != (C, (Hq + 2 * Hkv) * D):
+        raise ValueError("w_qkv must be [C, (Hq + 2 Hkv) D]")
+    q, k, v = _split_qkv(x.reshape(B * T, C) @ w, B, T, Hq, Hkv, D)
+    if rope_on:
+        q = rope(q, base, pos0)
+        k = rope(k, base, pos0)
+    return q, k, v
+
+
+def qkv_proj_bwd(x, w_qkv, dq, dk, dv):
+    """Gradients of the QKV projection from dq, dk, dv (w.r.t. the projections before RoPE):
+    dx [B, T, C] = [dq | dk | dv] w_qkv^T and dw_qkv = x^T [dq | dk | dv]."""
+    x, w = _f64(x), _f64(w_qkv)
+    dq, dk, dv = _f64(dq), _f64(dk), _f64(dv)
+    B, T, C = x.shape
+    g = np.concatenate([dq.reshape(B * T, -1), dk.reshape(B * T, -1), dv.reshape(B * T, -1)], axis=1)
+    if g.shape[1] != w.shape[1]:
+        raise ValueError("gradient widths do not match w_qkv")
+    dx = (g @ w.T).reshape(B, T, C)
+    dw = x.reshape(B * T, C).T @ g
+    return dx, dw
