@@ -13,6 +13,9 @@ built, or the tensors are not on a ROCm device, the calls raise.
                          -> (dq, dk, dv) with dq, dk for the tensors before RoPE
     attn_decode(q, k_cache, v_cache, scale=None, ...)         -> (o, lse) for the last Tq rows
     attn_fwd_noncausal / attn_bwd_noncausal                   -> as attn_fwd / attn_bwd, no mask
+    gemm(a, b, trans_a=False, trans_b=False, out=None)        -> op(a) @ op(b)
+    qkv_proj(x, w_qkv, Hq, Hkv, D, rope=True, base=1e4, ...)  -> (q, k, v) [B, T, H, D]
+    qkv_proj_bwd(x, w_qkv, dq, dk, dv)                         -> (dx, dw_qkv)
 
 Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
 dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
@@ -27,7 +30,8 @@ import torch
 
 __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
-           "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "gemm",
+           "qkv_proj", "qkv_proj_bwd", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
@@ -81,6 +85,12 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_decode.restype = ci
+    L.gemm.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, vp]
+    L.gemm.restype = ci
+    L.qkv_proj.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, cd, ci, vp]
+    L.qkv_proj.restype = ci
+    L.qkv_proj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    L.qkv_proj_bwd.restype = ci
     L.euler_attn_status_string.argtypes = [ci]
     L.euler_attn_status_string.restype = ctypes.c_char_p
     L.euler_attn_version.argtypes = []
@@ -392,3 +402,71 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float 
                                B, Tq, Tk, Hq, Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
     _raise(st, "attn_decode")
     return o, l
+
+
+def gemm(a: torch.Tensor, b: torch.Tensor, trans_a: bool = False, trans_b: bool = False,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """op(a) @ op(b) for contiguous 2-D tensors (op transposes when its flag is set)."""
+    _check("a", a, 2)
+    _check("b", b, 2, a.device, a.dtype)
+    M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
+    Kb, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    if K != Kb:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, Kb))
+    c = torch.empty((M, N), device=a.device, dtype=a.dtype) if out is None else out
+    _check("out", c, 2, a.device, a.dtype)
+    if tuple(c.shape) != (M, N):
+        raise ValueError("out must be [%d, %d]" % (M, N))
+    with torch.cuda.device(a.device):
+        st = lib().gemm(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, a.shape[1], b.shape[1], N,
+                        int(bool(trans_a)), int(bool(trans_b)), _dtype_code(a), _stream(a.device))
+    _raise(st, "gemm")
+    return c
+
+
+def qkv_proj(x: torch.Tensor, w_qkv: torch.Tensor, Hq: int, Hkv: int, D: int, rope: bool = True,
+             base: float = 10000.0, pos0: int = 0, q: torch.Tensor | None = None,
+             k: torch.Tensor | None = None, v: torch.Tensor | None = None):
+    """q, k, v = x Wq, x Wk, x Wv from x [B, T, C] and w_qkv [C, (Hq + 2 Hkv) D], as
+    [B, T, H, D]; with rope, q and k are rotated (as rope_apply) before they are stored."""
+    _check("x", x, 3)
+    _check("w_qkv", w_qkv, 2, x.device, x.dtype)
+    B, T, C = x.shape
+    outs = []
+    for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        t = torch.empty((B, T, H, D), device=x.device, dtype=x.dtype) if t is None else t
+        _check(name, t, 4, x.device, x.dtype)
+        if tuple(t.shape) != (B, T, H, D):
+            raise ValueError("%s must be [B, T, %d, D]" % (name, H))
+        outs.append(t)
+    with torch.cuda.device(x.device):
+        st = lib().qkv_proj(x.data_ptr(), w_qkv.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                            outs[2].data_ptr(), B, T, C, Hq, Hkv, D, _dtype_code(x), int(bool(rope)),
+                            float(base), int(pos0), _stream(x.device))
+    _raise(st, "qkv_proj")
+    return tuple(outs)
+
+
+def qkv_proj_bwd(x: torch.Tensor, w_qkv: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+                 dv: torch.Tensor, dx: torch.Tensor | None = None, dw_qkv: torch.Tensor | None = None):
+    """dx = [dq | dk | dv] w_qkv^T and dw_qkv = x^T [dq | dk | dv] (dq, dk: gradients of the
+    projections before RoPE).  Returns (dx, dw_qkv)."""
+    _check("x", x, 3)
+    _check("w_qkv", w_qkv, 2, x.device, x.dtype)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, 4, x.device, x.dtype)
+    B, T, C = x.shape
+    Hq, D = dq.shape[2], dq.shape[3]
+    Hkv = dk.shape[2]
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w_qkv) if dw_qkv is None else dw_qkv
+    _check("dx", dx, 3, x.device, x.dtype)
+    _check("dw_qkv", dw, 2, x.device, x.dtype)
+    if dx.shape != x.shape or dw.shape != w_qkv.shape:
+        raise ValueError("dx / dw_qkv must match x / w_qkv")
+    with torch.cuda.device(x.device):
+        st = lib().qkv_proj_bwd(x.data_ptr(), w_qkv.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                dx.data_ptr(), dw.data_ptr(), B, T, C, Hq, Hkv, D, _dtype_code(x),
+                                _stream(x.device))
+    _raise(st, "qkv_proj_bwd")
+    return dx, dw

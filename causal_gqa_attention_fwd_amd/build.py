@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libeuler_attn.so")
-SOURCES = ["api.hip", "rope.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+SOURCES = ["api.hip", "rope.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -370,3 +370,111 @@ ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* 
 }
 
 }  // extern "C"
+
+namespace {
+
+// Bytes spanned by `rows` rows of `cols` elements with leading dimension ld.
+size_t span_bytes(long long rows, long long cols, long long ld, size_t es) {
+    return (size_t)(((rows - 1) * ld + cols) * (long long)es);
+}
+
+// The QKV projection's three column segments (Q, K, V) of the [B*T, (Hq + 2 Hkv) D] product.
+void qkv_segs(ea::GemmSeg* s, const void* q, const void* k, const void* v, int Hq, int Hkv, int D) {
+    s[0] = ea::GemmSeg{q, (long long)Hq * D, 0};
+    s[1] = ea::GemmSeg{k, (long long)Hkv * D, Hq * D};
+    s[2] = ea::GemmSeg{v, (long long)Hkv * D, (Hq + Hkv) * D};
+}
+
+ea_status check_qkv_sizes(int B, int T, int C, int Hq, int Hkv, int D, ea_dtype dt) {
+    if (B < 1 || T < 1 || C < 1 || Hq < 1 || Hkv < 1 || D < 2 || Hq % Hkv != 0) return EA_ERR_INVALID_ARG;
+    if (!dtype_ok(dt)) return EA_ERR_UNSUPPORTED;
+    const int epc = (int)(16 / elem_size(dt));
+    if (C % epc != 0 || D % epc != 0 || D > 256) return EA_ERR_UNSUPPORTED;
+    if ((long long)B * T > (1LL << 30) || (long long)(Hq + 2 * Hkv) * D > (1 << 24) || C > (1 << 24))
+        return EA_ERR_UNSUPPORTED;
+    return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+               int ldc, int trans_a, int trans_b, ea_dtype dt, hipStream_t stream) {
+    if (!a || !b || !c) return EA_ERR_NULL;
+    if (M < 1 || N < 1 || K < 1) return EA_ERR_INVALID_ARG;
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return EA_ERR_INVALID_ARG;
+    if (!dtype_ok(dt) || (trans_a == 1 && trans_b == 1)) return EA_ERR_UNSUPPORTED;
+    const int epc = (int)(16 / elem_size(dt));
+    // 16-byte chunks along every contiguous dimension that is loaded or stored.
+    if (N % epc != 0 || ((trans_a == 0 || trans_b == 1) && K % epc != 0) || (trans_a == 1 && M % epc != 0))
+        return EA_ERR_UNSUPPORTED;
+    const long long a_rows = trans_a ? K : M, a_cols = trans_a ? M : K;
+    const long long b_rows = trans_b ? N : K, b_cols = trans_b ? K : N;
+    if (lda < a_cols || ldb < b_cols || ldc < N) return EA_ERR_INVALID_ARG;
+    if (lda % epc || ldb % epc || ldc % epc || !aligned16(a) || !aligned16(b) || !aligned16(c))
+        return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const Range rc = range(c, span_bytes(M, N, ldc, es));
+    if (overlap(rc, range(a, span_bytes(a_rows, a_cols, lda, es))) ||
+        overlap(rc, range(b, span_bytes(b_rows, b_cols, ldb, es))))
+        return EA_ERR_ALIAS;
+    const ea::GemmSeg sa{a, lda, 0}, sb{b, ldb, 0}, sc{c, ldc, 0};
+    return from_hip(ea::launch_gemm(&sa, 1, &sb, 1, &sc, 1, M, N, K, trans_a, trans_b,
+                                    static_cast<ea::IoType>(dt), nullptr, stream));
+}
+
+ea_status qkv_proj(const void* x, const void* w_qkv, void* q, void* k, void* v, int B, int T,
+                   int C, int Hq, int Hkv, int D, ea_dtype dt, int rope, double base, int pos0,
+                   hipStream_t stream) {
+    if (!x || !w_qkv || !q || !k || !v) return EA_ERR_NULL;
+    ea_status st = check_qkv_sizes(B, T, C, Hq, Hkv, D, dt);
+    if (st != EA_OK) return st;
+    if (rope != 0 && rope != 1) return EA_ERR_INVALID_ARG;
+    if (rope && (st = check_rope_args(base, pos0, T)) != EA_OK) return st;
+    for (const void* p : {x, w_qkv, static_cast<const void*>(q), static_cast<const void*>(k),
+                          static_cast<const void*>(v)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const long long M = (long long)B * T, N = (long long)(Hq + 2 * Hkv) * D;
+    const Range ins[] = {range(x, (size_t)(M * C) * es), range(w_qkv, (size_t)(C * N) * es)};
+    const Range outs[] = {range(q, (size_t)(M * Hq * D) * es), range(k, (size_t)(M * Hkv * D) * es),
+                          range(v, (size_t)(M * Hkv * D) * es)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    const ea::GemmSeg sa{x, C, 0}, sb{w_qkv, N, 0};
+    ea::GemmSeg sc[3];
+    qkv_segs(sc, q, k, v, Hq, Hkv, D);
+    const ea::GemmRope r{0x3, T, D, pos0, base};
+    return from_hip(ea::launch_gemm(&sa, 1, &sb, 1, sc, 3, (int)M, (int)N, C, 0, 0,
+                                    static_cast<ea::IoType>(dt), rope ? &r : nullptr, stream));
+}
+
+ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                       const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                       int Hkv, int D, ea_dtype dt, hipStream_t stream) {
+    if (!x || !w_qkv || !dq || !dk || !dv || !dx || !dw_qkv) return EA_ERR_NULL;
+    ea_status st = check_qkv_sizes(B, T, C, Hq, Hkv, D, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {x, w_qkv, dq, dk, dv, static_cast<const void*>(dx), static_cast<const void*>(dw_qkv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const long long M = (long long)B * T, N = (long long)(Hq + 2 * Hkv) * D;
+    const Range ins[] = {range(x, (size_t)(M * C) * es), range(w_qkv, (size_t)(C * N) * es),
+                         range(dq, (size_t)(M * Hq * D) * es), range(dk, (size_t)(M * Hkv * D) * es),
+                         range(dv, (size_t)(M * Hkv * D) * es)};
+    const Range outs[] = {range(dx, (size_t)(M * C) * es), range(dw_qkv, (size_t)(C * N) * es)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    ea::GemmSeg g[3];
+    qkv_segs(g, dq, dk, dv, Hq, Hkv, D);
+    // dx = [dq | dk | dv] W^T: A split along K, B = W stored [C, N] = op(B)^T.
+    const ea::GemmSeg wb{w_qkv, N, 0}, sdx{dx, C, 0};
+    hipError_t e = ea::launch_gemm(g, 3, &wb, 1, &sdx, 1, (int)M, C, (int)N, 0, 1,
+                                   static_cast<ea::IoType>(dt), nullptr, stream);
+    if (e != hipSuccess) return from_hip(e);
+    // dW = x^T [dq | dk | dv]: A = x stored [M, C] = op(A)^T, B split along N.
+    const ea::GemmSeg xa{x, C, 0}, sdw{dw_qkv, N, 0};
+    return from_hip(ea::launch_gemm(&xa, 1, g, 3, &sdw, 1, C, (int)N, (int)M, 1, 0,
+                                    static_cast<ea::IoType>(dt), nullptr, stream));
+}
+
+}  // extern "C"

@@ -67,4 +67,24 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, void*
                               void* workspace, int B, int Tq, int Tk, int Hq, int Hkv, int D,
                               float scale, IoType dt, hipStream_t stream);
 
+// Matrix product C = op(A) op(B) (gemm.hip).  A may be split along K, B and C along N, into up
+// to kGemmMaxSeg segments (start = first index of the segment along the split dimension,
+// ld = leading dimension in elements; the first segment starts at 0).  trans_a / trans_b:
+// (0, 0), (0, 1) or (1, 0).  With rope, the column pairs of the C segments in rope->mask are
+// rotated as heads of rope->D columns at position pos0 + (m mod T).
+constexpr int kGemmMaxSeg = 3;
+struct GemmSeg {
+    const void* p;
+    long long ld;
+    int start;
+};
+struct GemmRope {
+    int mask;
+    int T, D, pos0;
+    double base;
+};
+hipError_t launch_gemm(const GemmSeg* a, int na, const GemmSeg* b, int nb, const GemmSeg* c,
+                       int nc, int M, int N, int K, int trans_a, int trans_b, IoType dt,
+                       const GemmRope* rope, hipStream_t stream);
+
 }  // namespace ea

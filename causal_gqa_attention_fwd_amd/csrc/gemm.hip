@@ -1,0 +1,395 @@
+// gemm.hip -- C = op(A) op(B) on the matrix cores (gfx950), for the projections on either
+// side of the attention: the QKV projection (with RoPE on Q and K applied in the epilogue)
+// and the output projection, forward and backward.
+//
+// The pages do these steps with a matrix library ("Show HN: NanoEuler", section 4; "Tiny
+// Hackable CUDA Language Model Implementation", sections 1 and 3: the attention result is
+// projected back to the model dimension, matrix products go to BLAS).  Here they are the
+// library's own kernels, tiled for 64-wide wavefronts and LDS.
+//
+// Layout: every matrix is row-major with a leading dimension.  op(A) is [M, K]: A stored as
+// [M, K] (trans_a = 0) or [K, M] (trans_a = 1); op(B) is [K, N]: B stored as [K, N]
+// (trans_b = 0) or [N, K] (trans_b = 1).  C is [M, N], fp32 accumulation, one rounding to
+// the I/O dtype.  A may be split along K, and B and C along N, into up to three segments,
+// each with its own base pointer and leading dimension: the QKV projection writes Q, K and
+// V as three separate [B, T, H, D] tensors from one product, and its backward reads the
+// three gradients as one operand.
+//
+// Work split: a workgroup computes a BM x BN tile of C with WM x WN waves; each wave owns
+// (BM/WM) x (BN/WN) as 32 x 32 matrix-core blocks.  The MFMA computes C^T = op(B)^T op(A)^T,
+// so a lane holds one row m of C and 16 of its columns in groups of four consecutive
+// columns: stores are 8 (bf16) or 16 (fp32) bytes, and the two columns of a RoPE pair sit
+// in one lane.  The contraction index of a 32-deep block follows the accumulator order
+// (ea_common.h): an operand whose rows are K-contiguous is read with two 8-byte LDS reads
+// per fragment, an operand whose rows run along K is read with the transposing LDS read.
+// Tiles go HBM -> registers -> LDS through two register sets (bf16) and a double-buffered
+// LDS, one barrier per K tile.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+
+#include "ea_common.h"
+#include "ea_kernels.h"
+
+namespace ea {
+namespace {
+
+struct Seg {
+    const void* p;
+    long long ld;  // leading dimension in elements
+    int start;     // first index (along K for A, along N for B and C) of this segment
+};
+
+struct GemmArgs {
+    Seg a[kGemmMaxSeg];  // A segments along K (trans_a = 0); unused segments start at INT_MAX
+    Seg b[kGemmMaxSeg];  // B segments along N (trans_b = 0)
+    Seg c[kGemmMaxSeg];  // C segments along N
+    int M, N, K;
+    int tiles_n;         // ceil(N / BN)
+    int rope_mask;       // bit s: rotate the column pairs of C segment s (heads of rope_D)
+    int rope_T, rope_D, rope_pos0;
+    RopeFreq f;
+};
+
+// Segments as plain values (no array indexed at run time, which would live in scratch).
+template <typename T>
+struct SegV {
+    const T* p0;
+    const T* p1;
+    const T* p2;
+    long long ld0, ld1, ld2;
+    int st1, st2;
+    __device__ inline explicit SegV(const Seg* s)
+        : p0(static_cast<const T*>(s[0].p)), p1(static_cast<const T*>(s[1].p)),
+          p2(static_cast<const T*>(s[2].p)), ld0(s[0].ld), ld1(s[1].ld), ld2(s[2].ld),
+          st1(s[1].start), st2(s[2].start) {}
+    // Address of element (r, x) where x runs along the split dimension and r across it.
+    __device__ inline const T* at(long long r, int x) const {
+        if (x >= st2) return p2 + r * ld2 + (x - st2);
+        if (x >= st1) return p1 + r * ld1 + (x - st1);
+        return p0 + r * ld0 + x;
+    }
+    __device__ inline int index(int x) const { return (x >= st1 ? 1 : 0) + (x >= st2 ? 1 : 0); }
+};
+
+// Fragment of KPL contraction elements from a row whose elements run along K (p points at
+// the start of a 32-deep block): element e <-> k = acc_row(ps * KPL + e, half).
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_k_frag(const T* p, int ps);
+
+template <>
+__device__ inline bf16x8 load_k_frag<bf16>(const bf16* p, int ps) {
+    const int h = __lane_id() >> 5;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + 16 * ps + 4 * h);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16 * ps + 8 + 4 * h);
+    bf16x8 f;
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    return f;
+}
+
+template <>
+__device__ inline float load_k_frag<float>(const float* p, int ps) {
+    return p[acc_row(ps, __lane_id() >> 5)];
+}
+
+template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
+struct GemmCfg {
+    static constexpr int KPL = Mfma<T>::KPL;
+    static constexpr int EPC = 16 / sizeof(T);
+    static constexpr int BK = sizeof(T) == 2 ? 64 : 32;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = 64 * NW;
+    static constexpr int MB = BM / WM / 32;  // 32-row blocks per wave
+    static constexpr int NB = BN / WN / 32;  // 32-column blocks per wave
+    static constexpr int PS = 16 / KPL;      // MFMA steps per 32-deep block
+    static constexpr int KB = BK / 32;
+    // A tile: [BM][BK] (trans_a = 0, row = m) or [BK][BM] (trans_a = 1, row = k); likewise B:
+    // [BK][BN] (trans_b = 0, row = k) or [BN][BK] (trans_b = 1, row = n).  16 bytes of padding
+    // per row.
+    static constexpr int A_ROWS = TA ? BK : BM, A_COLS = TA ? BM : BK;
+    static constexpr int B_ROWS = TB ? BN : BK, B_COLS = TB ? BK : BN;
+    static constexpr int A_STRIDE = A_COLS + EPC, B_STRIDE = B_COLS + EPC;
+    static constexpr int A_SIZE = A_ROWS * A_STRIDE, B_SIZE = B_ROWS * B_STRIDE;
+    static constexpr int A_CPR = A_COLS / EPC, B_CPR = B_COLS / EPC;  // chunks per tile row
+    static constexpr int NCA = (A_ROWS * A_CPR + NT - 1) / NT;       // chunks per thread
+    static constexpr int NCB = (B_ROWS * B_CPR + NT - 1) / NT;
+    static constexpr size_t LDS_BYTES = 2 * (size_t)(A_SIZE + B_SIZE) * sizeof(T);
+    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tiling");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
+    using C = GemmCfg<T, TA, TB, BM, BN, WM, WN>;
+    using M_ = Mfma<T>;
+    using frag = typename M_::frag;
+    constexpr int EPC = C::EPC;
+
+    __shared__ __attribute__((aligned(16))) T As[2 * C::A_SIZE];
+    __shared__ __attribute__((aligned(16))) T Bs[2 * C::B_SIZE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int wm = w / WN, wn = w % WN;
+    const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+    const int nk = (K + C::BK - 1) / C::BK;
+    const SegV<T> sa_(g.a), sb_(g.b);
+
+    // Staging of one K tile (HBM -> registers), then registers -> LDS.  Rows past M or N
+    // load a real row (clamped): they only feed outputs that are never stored.  Elements
+    // past K load zeros: they would otherwise enter valid outputs.
+    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    struct Stg {
+        Vec16<T> a[C::NCA], b[C::NCB];
+    };
+    Stg sa;
+    [[maybe_unused]] Stg sb;
+    auto fetch = [&](Stg& st, int kt) {
+        const int k0 = kt * C::BK;
+#pragma unroll
+        for (int n = 0; n < C::NCA; ++n) {
+            const int u = tid + n * C::NT;
+            if ((C::A_ROWS * C::A_CPR) % C::NT == 0 || u < C::A_ROWS * C::A_CPR) {
+                const int row = u / C::A_CPR, cc = u % C::A_CPR;
+                int m, k;
+                if constexpr (TA == 0) {
+                    m = min(m0 + row, M - 1);
+                    k = k0 + cc * EPC;
+                } else {
+                    k = k0 + row;
+                    m = min(m0 + cc * EPC, M - EPC);
+                }
+                if (k < K) {
+                    st.a[n] = ld16(TA == 0 ? sa_.at(m, k) : sa_.p0 + (long long)k * sa_.ld0 + m);
+                } else {
+                    st.a[n] = zero16<T>();
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < C::NCB; ++n) {
+            const int u = tid + n * C::NT;
+            if ((C::B_ROWS * C::B_CPR) % C::NT == 0 || u < C::B_ROWS * C::B_CPR) {
+                const int row = u / C::B_CPR, cc = u % C::B_CPR;
+                int nn, k;
+                if constexpr (TB == 0) {
+                    k = k0 + row;
+                    nn = min(n0 + cc * EPC, N - EPC);
+                } else {
+                    nn = min(n0 + row, N - 1);
+                    k = k0 + cc * EPC;
+                }
+                if (k < K) {
+                    st.b[n] = ld16(TB == 0 ? sb_.at(k, nn) : sb_.p0 + (long long)nn * sb_.ld0 + k);
+                } else {
+                    st.b[n] = zero16<T>();
+                }
+            }
+        }
+    };
+    auto commit = [&](const Stg& st, int buf) {
+#pragma unroll
+        for (int n = 0; n < C::NCA; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < C::A_ROWS * C::A_CPR) {
+                const int row = u / C::A_CPR, cc = u % C::A_CPR;
+                st16(&As[buf * C::A_SIZE + row * C::A_STRIDE + cc * EPC], st.a[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < C::NCB; ++n) {
+            const int u = tid + n * C::NT;
+            if (u < C::B_ROWS * C::B_CPR) {
+                const int row = u / C::B_CPR, cc = u % C::B_CPR;
+                st16(&Bs[buf * C::B_SIZE + row * C::B_STRIDE + cc * EPC], st.b[n]);
+            }
+        }
+    };
+
+    f32x16 acc[C::MB][C::NB];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = zero_acc();
+
+    const int wrow = wm * (BM / WM), wcol = wn * (BN / WN);
+    auto compute = [&](int buf) {
+        const T* at = As + buf * C::A_SIZE;
+        const T* bt = Bs + buf * C::B_SIZE;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+            for (int ps = 0; ps < C::PS; ++ps) {
+                frag fa[C::MB], fb[C::NB];
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) {
+                    if constexpr (TA == 0)
+                        fa[mb] = load_k_frag<T>(at + (wrow + mb * 32 + l32) * C::A_STRIDE + kb * 32, ps);
+                    else
+                        fa[mb] = load_rows_frag<T>(at, C::A_STRIDE, kb * 32, ps, wrow + mb * 32);
+                }
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    if constexpr (TB == 1)
+                        fb[nb] = load_k_frag<T>(bt + (wcol + nb * 32 + l32) * C::B_STRIDE + kb * 32, ps);
+                    else
+                        fb[nb] = load_rows_frag<T>(bt, C::B_STRIDE, kb * 32, ps, wcol + nb * 32);
+                }
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = M_::mma(fb[nb], fa[mb], acc[mb][nb]);
+            }
+        }
+    };
+
+    // K tile s sits in register set s % NSET until it is committed at the start of step
+    // s - 1; the set is then refilled with tile s + NSET.
+    fetch(sa, 0);
+    commit(sa, 0);
+    if constexpr (NSET == 2) {
+        if (nk > 1) fetch(sb, 1);
+        if (nk > 2) fetch(sa, 2);
+    } else {
+        if (nk > 1) fetch(sa, 1);
+    }
+    auto step = [&](int kt, Stg& nxt) {
+        __syncthreads();  // tile kt visible in buffer kt&1; buffer (kt+1)&1 free
+        if (kt + 1 < nk) {
+            commit(nxt, (kt + 1) & 1);
+            if (kt + 1 + NSET < nk) fetch(nxt, kt + 1 + NSET);
+        }
+        compute(kt & 1);
+    };
+    if constexpr (NSET == 2) {
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, sb);
+            if (kt + 1 < nk) step(kt + 1, sa);
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) step(kt, sa);
+    }
+
+    // Epilogue: lane = row m, registers 4*a4 .. 4*a4+3 of block nb = columns
+    // wcol + nb*32 + 8*a4 + 4*h + 0..3.
+    const SegV<T> sc_(g.c);
+    const int rope_mask = g.rope_mask;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+        const int m = m0 + wrow + mb * 32 + l32;
+        if (m >= M) continue;
+        const int t = rope_mask ? m % g.rope_T : 0;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int n = n0 + wcol + nb * 32 + 8 * a4 + 4 * h;
+                if (n >= N) continue;
+                const int s = sc_.index(n);
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc[mb][nb][4 * a4 + e];
+                if ((rope_mask >> s) & 1) {
+                    // Pairs (d, d+1), d even, of the head containing column n.
+                    const int d0 = (n - (s == 2 ? sc_.st2 : (s == 1 ? sc_.st1 : 0))) % g.rope_D;
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        float co, sn;
+                        rope_cos_sin((double)g.rope_pos0 + (double)t, g.f.theta[(d0 + e) >> 1], &co, &sn);
+                        const float x0 = x[e], x1 = x[e + 1];
+                        x[e] = x0 * co - x1 * sn;
+                        x[e + 1] = x0 * sn + x1 * co;
+                    }
+                }
+                T* cp = const_cast<T*>(sc_.at(m, n));
+                if constexpr (sizeof(T) == 2) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+                    *reinterpret_cast<bf16x4*>(cp) = v;
+                } else {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = x[e];
+                    *reinterpret_cast<f32x4*>(cp) = v;
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(GemmArgs g, hipStream_t stream) {
+    g.tiles_n = (g.N + BN - 1) / BN;
+    const long long blocks = (long long)((g.M + BM - 1) / BM) * g.tiles_n;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<T, TA, TB, BM, BN, WM, WN>), dim3((unsigned)blocks),
+                       dim3(64 * WM * WN), 0, stream, g);
+    return hipGetLastError();
+}
+
+// Tile shape: 128 x 128 (4 waves of 64 x 64) when that still gives every CU two tiles,
+// else 64 x 64 (4 waves of 32 x 32) for more, smaller workgroups.
+template <typename T, int TA, int TB>
+hipError_t launch_t(const GemmArgs& g, hipStream_t stream) {
+    const long long big = (long long)((g.M + 127) / 128) * ((g.N + 127) / 128);
+    if (big >= 512) return launch_cfg<T, TA, TB, 128, 128, 2, 2>(g, stream);
+    return launch_cfg<T, TA, TB, 64, 64, 2, 2>(g, stream);
+}
+
+template <typename T>
+hipError_t launch_dt(const GemmArgs& g, int ta, int tb, hipStream_t stream) {
+    if (ta == 0 && tb == 0) return launch_t<T, 0, 0>(g, stream);
+    if (ta == 0 && tb == 1) return launch_t<T, 0, 1>(g, stream);
+    if (ta == 1 && tb == 0) return launch_t<T, 1, 0>(g, stream);
+    return hipErrorInvalidValue;
+}
+
+void fill_segs(Seg* dst, const GemmSeg* src, int n) {
+    for (int s = 0; s < kGemmMaxSeg; ++s) {
+        if (s < n) {
+            dst[s].p = src[s].p;
+            dst[s].ld = src[s].ld;
+            dst[s].start = src[s].start;
+        } else {
+            dst[s].p = src[0].p;
+            dst[s].ld = src[0].ld;
+            dst[s].start = INT_MAX;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmSeg* a, int na, const GemmSeg* b, int nb, const GemmSeg* c,
+                       int nc, int M, int N, int K, int trans_a, int trans_b, IoType dt,
+                       const GemmRope* rope, hipStream_t stream) {
+    GemmArgs g{};
+    fill_segs(g.a, a, na);
+    fill_segs(g.b, b, nb);
+    fill_segs(g.c, c, nc);
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.rope_mask = 0;
+    g.rope_T = 1;
+    g.rope_D = 2;
+    if (rope != nullptr) {
+        g.rope_mask = rope->mask;
+        g.rope_T = rope->T;
+        g.rope_D = rope->D;
+        g.rope_pos0 = rope->pos0;
+        fill_rope_freq(&g.f, rope->D, rope->base);
+    }
+    return dt == kF32 ? launch_dt<float>(g, trans_a, trans_b, stream)
+                      : launch_dt<bf16>(g, trans_a, trans_b, stream);
+}
+
+}  // namespace ea

@@ -181,3 +181,21 @@ def make_decode_inputs(w: DecodeWorkload | str) -> dict:
     tdt = torch_dtype(w.dtype)
     return {"q": torch.from_numpy(q).to(tdt), "k": torch.from_numpy(k).to(tdt), "v": torch.from_numpy(v).to(tdt)}
 
+
+
+def make_proj_inputs(w: Workload | str, seed_offset: int = 500) -> dict:
+    """Seeded inputs of the projections around one attention layer of workload w: hidden
+    states x [B, T, C] and upstream gradient dy [B, T, C] ~ N(0, 1), and random-init weights
+    w_qkv [C, (Hq + 2 Hkv) D] and w_o [Hq D, C] ~ N(0, 1/C) (model dimension C = Hq D),
+    drawn in that order from ``default_rng(seed + seed_offset)`` in float32, then cast to the
+    workload's dtype.  There are no trained weights behind them."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    C = w.Hq * w.D
+    rng = np.random.default_rng(w.seed + seed_offset)
+    x = rng.standard_normal((w.B, w.T, C), dtype=np.float32)
+    wq = rng.standard_normal((C, (w.Hq + 2 * w.Hkv) * w.D), dtype=np.float32) * np.float32(1.0 / math.sqrt(C))
+    wo = rng.standard_normal((w.Hq * w.D, C), dtype=np.float32) * np.float32(1.0 / math.sqrt(C))
+    dy = rng.standard_normal((w.B, w.T, C), dtype=np.float32)
+    tdt = torch_dtype(w.dtype)
+    return {k: torch.from_numpy(a).to(tdt) for k, a in (("x", x), ("w_qkv", wq), ("w_o", wo), ("dy", dy))}

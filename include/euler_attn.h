@@ -217,6 +217,55 @@ ea_status attn_bwd_rope_main(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int D,
                              float scale, ea_dtype dt, hipStream_t stream);
 
+/*
+ * The projections on either side of the attention: the query, key and value heads, RoPE on
+ * queries and keys, no bias anywhere ("Show HN: NanoEuler", section 2); the attention result
+ * projected back to the model dimension ("Tiny Hackable CUDA Language Model Implementation",
+ * section 1); matrix products done by a matrix library beside the hand-written attention
+ * ("Show HN: NanoEuler", section 4).  All products accumulate in float32 and round once
+ * to dt.
+ *
+ * gemm -- C = op(A) op(B), row-major with leading dimensions (in elements).  op(A) is
+ * [M, K]: A is stored [M, K] (trans_a = 0, lda >= K) or [K, M] (trans_a = 1, lda >= M).
+ * op(B) is [K, N]: B is stored [K, N] (trans_b = 0, ldb >= N) or [N, K] (trans_b = 1,
+ * ldb >= K).  C is [M, N], ldc >= N, overwritten.  The layer uses y = x W (0, 0),
+ * dx = dy W^T (0, 1) and dW = x^T dy (1, 0) with W stored [in, out].
+ * Errors: NULL pointer (EA_ERR_NULL); M, N, K < 1, a leading dimension too small, a flag
+ * not 0/1 (EA_ERR_INVALID_ARG); unknown dt, trans_a = trans_b = 1, or a contiguous
+ * dimension that is not a multiple of 16 bytes (N always; K when trans_a = 0 or
+ * trans_b = 1; M when trans_a = 1) (EA_ERR_UNSUPPORTED); a pointer not 16-byte aligned or
+ * a leading dimension not a multiple of 16 bytes (EA_ERR_ALIGN); C overlapping A or B
+ * (EA_ERR_ALIAS).
+ */
+ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+               int ldc, int trans_a, int trans_b, ea_dtype dt, hipStream_t stream);
+
+/*
+ * qkv_proj -- the QKV projection of x [B, T, C] by w_qkv [C, (Hq + 2 Hkv) D] (row-major,
+ * columns: the Hq query heads, then the Hkv key heads, then the Hkv value heads, D each):
+ * q [B, T, Hq, D] = x Wq, k [B, T, Hkv, D] = x Wk, v [B, T, Hkv, D] = x Wv, in one launch.
+ * With rope = 1, q and k are rotated in the epilogue exactly as rope_apply (base, pos0)
+ * rotates them (angle in float64, reduced mod 2 pi, float32 sincos), from the float32 sums
+ * before the single rounding: q and k are then what attn_fwd takes.
+ * Errors: NULL pointer; B, T, C, Hq, Hkv < 1, Hq % Hkv != 0, D < 2, rope not 0/1, and with
+ * rope base <= 1 or not finite, pos0 < 0 or pos0 + T > 2^31 (EA_ERR_INVALID_ARG); unknown
+ * dt, C or D not a multiple of 16 bytes, D > 256 (EA_ERR_UNSUPPORTED); misalignment
+ * (EA_ERR_ALIGN); an output overlapping an input or another output (EA_ERR_ALIAS).
+ */
+ea_status qkv_proj(const void* x, const void* w_qkv, void* q, void* k, void* v, int B, int T,
+                   int C, int Hq, int Hkv, int D, ea_dtype dt, int rope, double base, int pos0,
+                   hipStream_t stream);
+
+/*
+ * qkv_proj_bwd -- gradients of the QKV projection: with dq, dk, dv the gradients of the
+ * projected q, k, v BEFORE RoPE (what attn_bwd_rope returns for q and k),
+ * dx [B, T, C] = [dq | dk | dv] w_qkv^T and dw_qkv [C, (Hq + 2 Hkv) D] = x^T [dq | dk | dv],
+ * both overwritten (two launches).  Sizes and errors as qkv_proj.
+ */
+ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                       const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                       int Hkv, int D, ea_dtype dt, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* euler_attn_status_string(ea_status s);
 

@@ -259,3 +259,62 @@ def test_binding_refuses_cpu_tensors():
         ea.attn_fwd(x, x[:, :, :1].contiguous(), x[:, :, :1].contiguous())
     with pytest.raises(RuntimeError):
         ea.attn_fwd_noncausal(x, x[:, :, :1].contiguous(), x[:, :, :1].contiguous())
+
+
+def gemm_call(L, a=fake(0), b=fake(1), c=fake(2), M=64, N=64, K=64, lda=None, ldb=None, ldc=None,
+              ta=0, tb=0, dt=BF16):
+    lda = (M if ta else K) if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return L.gemm(a, b, c, M, N, K, lda, ldb, ldc, ta, tb, dt, None)
+
+
+def test_gemm_validation(L):
+    for name in ("a", "b", "c"):
+        assert gemm_call(L, **{name: None}) == NULL, name
+    for kw in (dict(M=0), dict(N=0), dict(K=0), dict(ta=2), dict(tb=-1), dict(lda=32), dict(ldb=8),
+               dict(ldc=56), dict(ta=1, lda=32)):
+        assert gemm_call(L, **kw) == INVALID, kw
+    assert gemm_call(L, ta=1, tb=1) == UNSUP
+    assert gemm_call(L, dt=5) == UNSUP
+    assert gemm_call(L, N=60) == UNSUP                  # N not a multiple of 8 bf16 elements
+    assert gemm_call(L, K=60) == UNSUP                  # K along rows of A
+    assert gemm_call(L, M=60, ta=1) == UNSUP            # M along rows of A^T
+    assert gemm_call(L, lda=68) == ALIGN
+    assert gemm_call(L, c=fake(2) + 8) == ALIGN
+    assert gemm_call(L, c=fake(0) + 1024) == ALIAS      # C inside A
+    assert gemm_call(L, b=fake(2) + 64 * 64 * 2 - 16) == ALIAS
+
+
+def qkv(L, x=fake(0), w=fake(1), q=fake(2), k=fake(3), v=fake(4), B=2, T=16, C=64, Hq=4, Hkv=2, D=16,
+        dt=BF16, rope=1, base=1e4, pos0=0):
+    return L.qkv_proj(x, w, q, k, v, B, T, C, Hq, Hkv, D, dt, rope, base, pos0, None)
+
+
+def test_qkv_proj_validation(L):
+    for name in ("x", "w", "q", "k", "v"):
+        assert qkv(L, **{name: None}) == NULL, name
+    for kw in (dict(B=0), dict(T=0), dict(C=0), dict(Hq=3), dict(D=1), dict(rope=2), dict(base=1.0),
+               dict(base=float("nan")), dict(pos0=-1)):
+        assert qkv(L, **kw) == INVALID, kw
+    for kw in (dict(C=60), dict(D=12), dict(D=264), dict(dt=3)):
+        assert qkv(L, **kw) == UNSUP, kw
+    assert qkv(L, k=fake(3) + 4) == ALIGN
+    assert qkv(L, q=fake(0) + 256) == ALIAS             # q over x
+    assert qkv(L, v=fake(3) + 512) == ALIAS             # v over k
+
+
+def test_qkv_proj_bwd_validation(L):
+    def call(**kw):
+        a = dict(x=fake(0), w=fake(1), dq=fake(2), dk=fake(3), dv=fake(4), dx=fake(5), dw=fake(6), B=2, T=16,
+                 C=64, Hq=4, Hkv=2, D=16, dt=BF16)
+        a.update(kw)
+        return L.qkv_proj_bwd(a["x"], a["w"], a["dq"], a["dk"], a["dv"], a["dx"], a["dw"], a["B"], a["T"],
+                              a["C"], a["Hq"], a["Hkv"], a["D"], a["dt"], None)
+    for name in ("x", "w", "dq", "dk", "dv", "dx", "dw"):
+        assert call(**{name: None}) == NULL, name
+    assert call(Hq=3) == INVALID
+    assert call(C=20) == UNSUP
+    assert call(dx=fake(5) + 2) == ALIGN
+    assert call(dx=fake(1)) == ALIAS                    # dx over w
+    assert call(dw=fake(5) + 64) == ALIAS               # dw over dx
