@@ -13,11 +13,12 @@ head_dim 64, bf16 I/O (the blog's benchmark shape).
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--extra NAMES]
-                    [--decode NAMES] [--noncausal NAMES]
+                    [--decode NAMES] [--noncausal NAMES] [--proj NAMES]
 
 Besides the headline step, the line carries the other timed paths of the library: extra
-workloads of the same step ('extra'), attention against a KV cache ('decode') and the
-attention without the causal mask ('noncausal').
+workloads of the same step ('extra'), attention against a KV cache ('decode'), the
+attention without the causal mask ('noncausal') and the projections on either side of the
+attention, forward and backward ('projections').
 """
 from __future__ import annotations
 
@@ -293,6 +294,69 @@ def time_noncausal(name, steps, warmup, torch, ea, W):
             "bwd_tflops": round(10 * w.D * pairs / (bwd_us * 1e-6) / 1e12, 2)}
 
 
+def time_projections(name, steps, warmup, torch, ea, W):
+    """The projections around one attention layer of a workload (model dimension C = Hq D):
+    qkv_proj with RoPE (x [B*T, C] by w_qkv [C, (Hq + 2 Hkv) D]), the output projection
+    y = o W_o, its backward (do = dy W_o^T, dW_o = o^T dy) and qkv_proj_bwd (dx and dW_qkv).
+    Average microseconds per call from HIP events on the launch stream, and TFLOP/s at
+    2 M N K per product against the dense MFMA peak of the dtype."""
+    w = W.WORKLOADS[name]
+    log("[bench] projections of workload %s" % name)
+    inp = W.make_proj_inputs(w)
+    dev = torch.device("cuda", 0)
+    x, wq, wo, dy = (inp[k].to(dev) for k in ("x", "w_qkv", "w_o", "dy"))
+    B, T, C, Hq, Hkv, D = w.B, w.T, w.Hq * w.D, w.Hq, w.Hkv, w.D
+    M, Nq = B * T, (Hq + 2 * Hkv) * D
+    q = torch.empty((B, T, Hq, D), device=dev, dtype=x.dtype)
+    k = torch.empty((B, T, Hkv, D), device=dev, dtype=x.dtype)
+    v = torch.empty_like(k)
+    o = W.make_random((B * T, Hq * D), w.seed + 700, w.dtype).to(dev)
+    y = torch.empty((M, C), device=dev, dtype=x.dtype)
+    do = torch.empty_like(o)
+    dwo = torch.empty_like(wo)
+    dx = torch.empty_like(x)
+    dwq = torch.empty_like(wq)
+    L = ea.lib()
+    dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    p = lambda t: t.data_ptr()  # noqa: E731
+    calls = [
+        ("qkv_proj_rope", 2 * M * Nq * C, L.qkv_proj,
+         (p(x), p(wq), p(q), p(k), p(v), B, T, C, Hq, Hkv, D, dtc, 1, w.base, 0, stream)),
+        ("out_proj", 2 * M * C * Hq * D, L.gemm,
+         (p(o), p(wo), p(y), M, C, Hq * D, Hq * D, C, C, 0, 0, dtc, stream)),
+        ("out_proj_bwd_dx", 2 * M * C * Hq * D, L.gemm,
+         (p(dy), p(wo), p(do), M, Hq * D, C, C, C, Hq * D, 0, 1, dtc, stream)),
+        ("out_proj_bwd_dw", 2 * M * C * Hq * D, L.gemm,
+         (p(o), p(dy), p(dwo), Hq * D, C, M, Hq * D, C, C, 1, 0, dtc, stream)),
+        ("qkv_proj_bwd", 2 * 2 * M * Nq * C, L.qkv_proj_bwd,
+         (p(x), p(wq), p(q), p(k), p(v), p(dx), p(dwq), B, T, C, Hq, Hkv, D, dtc, stream)),
+    ]
+    out = {"config": dict(w.describe(), model_dim=C), "calls": steps, "kernels": {}}
+    total_us, total_flops = 0.0, 0
+    for cname, flops, fn, args in calls:
+        for _ in range(warmup):
+            if fn(*args) != 0:
+                raise RuntimeError("%s failed" % cname)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / steps
+        tf = flops / (us * 1e-6) / 1e12
+        total_us += us
+        total_flops += flops
+        out["kernels"][cname] = {"us_per_call": round(us, 2), "flops": flops, "tflops": round(tf, 2),
+                                 "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4)}
+    out["total_us"] = round(total_us, 2)
+    out["total_tflops"] = round(total_flops / (total_us * 1e-6) / 1e12, 2)
+    return out
+
+
 def cpu_baseline(w, W):
     """The oracle (plain float64 C++, OpenMP) on the host cores: one whole step of the same
     workload (RoPE on Q and K, forward, analytic backward, inverse RoPE on dQ and dK)."""
@@ -339,6 +403,9 @@ def main() -> int:
     ap.add_argument("--noncausal", default="blog_t1024,long_t8192",
                     help="comma-separated workloads run through attn_fwd_noncausal + attn_bwd_noncausal, "
                          "reported under 'noncausal'; empty to skip")
+    ap.add_argument("--proj", default="blog_t1024",
+                    help="comma-separated workloads whose QKV / output projections (forward and backward) "
+                         "are timed under 'projections'; empty to skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -405,6 +472,8 @@ def main() -> int:
     out["extra"] = extra
     out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                      for name in [x for x in args.decode.split(",") if x]}
+    out["projections"] = {name: time_projections(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
+                          for name in [x for x in args.proj.split(",") if x]}
     out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5), torch, ea, W)
                         for name in [x for x in args.noncausal.split(",") if x]}
     if not args.no_cpu_baseline:

@@ -64,11 +64,13 @@ struct SegV {
         : p0(static_cast<const T*>(s[0].p)), p1(static_cast<const T*>(s[1].p)),
           p2(static_cast<const T*>(s[2].p)), ld0(s[0].ld), ld1(s[1].ld), ld2(s[2].ld),
           st1(s[1].start), st2(s[2].start) {}
-    // Address of element (r, x) where x runs along the split dimension and r across it.
+    // Address of element (r, x) where x runs along the split dimension and r across it
+    // (selects, no branches: the loads that use it stay unconditional).
     __device__ inline const T* at(long long r, int x) const {
-        if (x >= st2) return p2 + r * ld2 + (x - st2);
-        if (x >= st1) return p1 + r * ld1 + (x - st1);
-        return p0 + r * ld0 + x;
+        const T* a0 = p0 + r * ld0 + x;
+        const T* a1 = p1 + r * ld1 + (x - st1);
+        const T* a2 = p2 + r * ld2 + (x - st2);
+        return x >= st2 ? a2 : (x >= st1 ? a1 : a0);
     }
     __device__ inline int index(int x) const { return (x >= st1 ? 1 : 0) + (x >= st2 ? 1 : 0); }
 };
@@ -142,17 +144,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     const int nk = (K + C::BK - 1) / C::BK;
     const SegV<T> sa_(g.a), sb_(g.b);
 
-    // Staging of one K tile (HBM -> registers), then registers -> LDS.  Rows past M or N
-    // load a real row (clamped): they only feed outputs that are never stored.  Elements
-    // past K load zeros: they would otherwise enter valid outputs.
+    // Staging of one K tile (HBM -> registers), then registers -> LDS.  Every load is
+    // unconditional, from a clamped address, so that the loads of later tiles stay in flight
+    // while earlier ones are committed.  Rows past M or N load a real row: they only feed
+    // outputs that are never stored.  Chunks past K load a real chunk too and are replaced
+    // by zeros at commit (bit n of ok clear), as they would otherwise enter valid outputs.
     constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    static_assert(C::NCA + C::NCB <= 32, "chunk mask");
     struct Stg {
         Vec16<T> a[C::NCA], b[C::NCB];
+        uint32_t ok;
     };
     Stg sa;
     [[maybe_unused]] Stg sb;
     auto fetch = [&](Stg& st, int kt) {
         const int k0 = kt * C::BK;
+        uint32_t ok = 0;
 #pragma unroll
         for (int n = 0; n < C::NCA; ++n) {
             const int u = tid + n * C::NT;
@@ -166,10 +173,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
                     k = k0 + row;
                     m = min(m0 + cc * EPC, M - EPC);
                 }
-                if (k < K) {
-                    st.a[n] = ld16(TA == 0 ? sa_.at(m, k) : sa_.p0 + (long long)k * sa_.ld0 + m);
+                ok |= (k < K ? 1u : 0u) << n;
+                if constexpr (TA == 0) {
+                    st.a[n] = ld16(sa_.at(m, min(k, K - EPC)));
                 } else {
-                    st.a[n] = zero16<T>();
+                    st.a[n] = ld16(sa_.p0 + (long long)min(k, K - 1) * sa_.ld0 + m);
                 }
             }
         }
@@ -186,13 +194,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
                     nn = min(n0 + row, N - 1);
                     k = k0 + cc * EPC;
                 }
-                if (k < K) {
-                    st.b[n] = ld16(TB == 0 ? sb_.at(k, nn) : sb_.p0 + (long long)nn * sb_.ld0 + k);
+                ok |= (k < K ? 1u : 0u) << (C::NCA + n);
+                if constexpr (TB == 0) {
+                    st.b[n] = ld16(sb_.at(min(k, K - 1), nn));
                 } else {
-                    st.b[n] = zero16<T>();
+                    st.b[n] = ld16(sb_.p0 + (long long)nn * sb_.ld0 + min(k, K - EPC));
                 }
             }
         }
+        st.ok = ok;
     };
     auto commit = [&](const Stg& st, int buf) {
 #pragma unroll
@@ -200,7 +210,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
             const int u = tid + n * C::NT;
             if (u < C::A_ROWS * C::A_CPR) {
                 const int row = u / C::A_CPR, cc = u % C::A_CPR;
-                st16(&As[buf * C::A_SIZE + row * C::A_STRIDE + cc * EPC], st.a[n]);
+                Vec16<T> v = st.a[n];
+                const uint32_t mk = 0u - ((st.ok >> n) & 1u);
+                v.raw &= u32x4{mk, mk, mk, mk};
+                st16(&As[buf * C::A_SIZE + row * C::A_STRIDE + cc * EPC], v);
             }
         }
 #pragma unroll
@@ -208,7 +221,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
             const int u = tid + n * C::NT;
             if (u < C::B_ROWS * C::B_CPR) {
                 const int row = u / C::B_CPR, cc = u % C::B_CPR;
-                st16(&Bs[buf * C::B_SIZE + row * C::B_STRIDE + cc * EPC], st.b[n]);
+                Vec16<T> v = st.b[n];
+                const uint32_t mk = 0u - ((st.ok >> (C::NCA + n)) & 1u);
+                v.raw &= u32x4{mk, mk, mk, mk};
+                st16(&Bs[buf * C::B_SIZE + row * C::B_STRIDE + cc * EPC], v);
             }
         }
     };
