@@ -406,6 +406,9 @@ def main() -> int:
     ap.add_argument("--proj", default="blog_t1024",
                     help="comma-separated workloads whose QKV / output projections (forward and backward) "
                          "are timed under 'projections'; empty to skip")
+    ap.add_argument("--only", default="",
+                    help="profiling aid: comma-separated subset of extra,decode,projections,noncausal to run "
+                         "WITHOUT the headline step (prints those sections only, not the benchmark line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -431,6 +434,25 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 5}))
+        return 0
+
+    if args.only:
+        # Kernel-trace runs of the secondary paths, so that their kernels (some shared with the
+        # headline step) appear in a profile by themselves.
+        want = set(x for x in args.only.split(",") if x)
+        out = {"only": sorted(want)}
+        if "decode" in want:
+            out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
+                             for name in [x for x in args.decode.split(",") if x]}
+        if "projections" in want:
+            out["projections"] = {name: time_projections(name, max(20, args.steps), max(3, args.warmup // 2),
+                                                         torch, ea, W)
+                                  for name in [x for x in args.proj.split(",") if x]}
+        if "noncausal" in want:
+            out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5),
+                                                     torch, ea, W)
+                                for name in [x for x in args.noncausal.split(",") if x]}
+        print(json.dumps(out), flush=True)
         return 0
 
     w, step, ms, wall, kern_us = time_workload(args.workload, args.steps, args.warmup, torch, ea, W)
