@@ -35,6 +35,8 @@
 namespace ea {
 namespace {
 
+constexpr int kXcds = 8;  // workgroups are dealt to the XCDs round-robin
+
 struct Seg {
     const void* p;
     long long ld;  // leading dimension in elements
@@ -46,7 +48,7 @@ struct GemmArgs {
     Seg b[kGemmMaxSeg];  // B segments along N (trans_b = 0)
     Seg c[kGemmMaxSeg];  // C segments along N
     int M, N, K;
-    int tiles_n;         // ceil(N / BN)
+    int tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
     int rope_mask;       // bit s: rotate the column pairs of C segment s (heads of rope_D)
     int rope_T, rope_D, rope_pos0;
     RopeFreq f;
@@ -138,7 +140,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const int wm = w / WN, wn = w % WN;
-    const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    // XCD-aware tile order: workgroup L runs on XCD L % 8, and XCD x takes a contiguous run of
+    // tiles (row-major over the tile grid), so the A rows and B columns its workgroups share
+    // are fetched into its own L2 rather than into all eight.
+    const int ntiles = g.tiles_m * g.tiles_n;
+    const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+    const int q8 = ntiles / kXcds, r8 = ntiles % kXcds;
+    const int tile = xcd < r8 ? xcd * (q8 + 1) + jx : r8 * (q8 + 1) + (xcd - r8) * q8 + jx;
+    const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
     const int nk = (K + C::BK - 1) / C::BK;
@@ -157,7 +166,66 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     };
     Stg sa;
     [[maybe_unused]] Stg sb;
-    auto fetch = [&](Stg& st, int kt) {
+    // Per-chunk source addresses that do not change along K, computed once (the K loop only
+    // adds its offset): A row / column bases (unless A is split along K, which takes the
+    // general path below), B bases with their segment's leading dimension.
+    const bool a_split_k = TA == 0 && sa_.st1 != INT_MAX;
+    const T* abase[C::NCA];
+    int aoff[C::NCA];
+    const T* bbase[C::NCB];
+    long long bld[C::NCB];
+    int boff[C::NCB];
+#pragma unroll
+    for (int n = 0; n < C::NCA; ++n) {
+        const int u = tid + n * C::NT;
+        const int row = u / C::A_CPR, cc = u % C::A_CPR;
+        if constexpr (TA == 0) {
+            abase[n] = sa_.p0 + (long long)min(m0 + row, M - 1) * sa_.ld0;
+            aoff[n] = cc * EPC;
+        } else {
+            abase[n] = sa_.p0 + min(m0 + cc * EPC, M - EPC);
+            aoff[n] = row;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < C::NCB; ++n) {
+        const int u = tid + n * C::NT;
+        const int row = u / C::B_CPR, cc = u % C::B_CPR;
+        if constexpr (TB == 0) {
+            const int nn = min(n0 + cc * EPC, N - EPC);
+            bbase[n] = sb_.at(0, nn);
+            bld[n] = nn >= sb_.st2 ? sb_.ld2 : (nn >= sb_.st1 ? sb_.ld1 : sb_.ld0);
+            boff[n] = row;
+        } else {
+            bbase[n] = sb_.p0 + (long long)min(n0 + row, N - 1) * sb_.ld0;
+            bld[n] = 1;
+            boff[n] = cc * EPC;
+        }
+    }
+    auto fetch_fast = [&](Stg& st, int kt) {
+        const int k0 = kt * C::BK;
+        uint32_t ok = 0;
+#pragma unroll
+        for (int n = 0; n < C::NCA; ++n) {
+            const int k = k0 + aoff[n];
+            ok |= (k < K ? 1u : 0u) << n;
+            if constexpr (TA == 0)
+                st.a[n] = ld16(abase[n] + min(k, K - EPC));
+            else
+                st.a[n] = ld16(abase[n] + (long long)min(k, K - 1) * sa_.ld0);
+        }
+#pragma unroll
+        for (int n = 0; n < C::NCB; ++n) {
+            const int k = k0 + boff[n];
+            ok |= (k < K ? 1u : 0u) << (C::NCA + n);
+            if constexpr (TB == 0)
+                st.b[n] = ld16(bbase[n] + (long long)min(k, K - 1) * bld[n]);
+            else
+                st.b[n] = ld16(bbase[n] + min(k, K - EPC));
+        }
+        st.ok = ok;
+    };
+    auto fetch_general = [&](Stg& st, int kt) {
         const int k0 = kt * C::BK;
         uint32_t ok = 0;
 #pragma unroll
@@ -204,16 +272,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         }
         st.ok = ok;
     };
-    auto commit = [&](const Stg& st, int buf) {
+    auto fetch = [&](Stg& st, int kt) {
+        if (a_split_k)
+            fetch_general(st, kt);
+        else
+            fetch_fast(st, kt);
+    };
+    // tail: this is the last K tile and K is not a multiple of BK (chunks past K -> zeros).
+    auto commit = [&](Stg& st, int buf, bool tail) {
+        if (tail) {
+#pragma unroll
+            for (int n = 0; n < C::NCA; ++n) {
+                const uint32_t mk = 0u - ((st.ok >> n) & 1u);
+                st.a[n].raw &= u32x4{mk, mk, mk, mk};
+            }
+#pragma unroll
+            for (int n = 0; n < C::NCB; ++n) {
+                const uint32_t mk = 0u - ((st.ok >> (C::NCA + n)) & 1u);
+                st.b[n].raw &= u32x4{mk, mk, mk, mk};
+            }
+        }
 #pragma unroll
         for (int n = 0; n < C::NCA; ++n) {
             const int u = tid + n * C::NT;
             if (u < C::A_ROWS * C::A_CPR) {
                 const int row = u / C::A_CPR, cc = u % C::A_CPR;
-                Vec16<T> v = st.a[n];
-                const uint32_t mk = 0u - ((st.ok >> n) & 1u);
-                v.raw &= u32x4{mk, mk, mk, mk};
-                st16(&As[buf * C::A_SIZE + row * C::A_STRIDE + cc * EPC], v);
+                st16(&As[buf * C::A_SIZE + row * C::A_STRIDE + cc * EPC], st.a[n]);
             }
         }
 #pragma unroll
@@ -221,13 +305,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
             const int u = tid + n * C::NT;
             if (u < C::B_ROWS * C::B_CPR) {
                 const int row = u / C::B_CPR, cc = u % C::B_CPR;
-                Vec16<T> v = st.b[n];
-                const uint32_t mk = 0u - ((st.ok >> (C::NCA + n)) & 1u);
-                v.raw &= u32x4{mk, mk, mk, mk};
-                st16(&Bs[buf * C::B_SIZE + row * C::B_STRIDE + cc * EPC], v);
+                st16(&Bs[buf * C::B_SIZE + row * C::B_STRIDE + cc * EPC], st.b[n]);
             }
         }
     };
+    const bool k_ragged = K % C::BK != 0;
 
     f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -269,7 +351,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     // K tile s sits in register set s % NSET until it is committed at the start of step
     // s - 1; the set is then refilled with tile s + NSET.
     fetch(sa, 0);
-    commit(sa, 0);
+    commit(sa, 0, k_ragged && nk == 1);
     if constexpr (NSET == 2) {
         if (nk > 1) fetch(sb, 1);
         if (nk > 2) fetch(sa, 2);
@@ -279,7 +361,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     auto step = [&](int kt, Stg& nxt) {
         __syncthreads();  // tile kt visible in buffer kt&1; buffer (kt+1)&1 free
         if (kt + 1 < nk) {
-            commit(nxt, (kt + 1) & 1);
+            commit(nxt, (kt + 1) & 1, k_ragged && kt + 2 == nk);
             if (kt + 1 + NSET < nk) fetch(nxt, kt + 1 + NSET);
         }
         compute(kt & 1);
@@ -344,7 +426,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(GemmArgs g, hipStream_t stream) {
     g.tiles_n = (g.N + BN - 1) / BN;
-    const long long blocks = (long long)((g.M + BM - 1) / BM) * g.tiles_n;
+    g.tiles_m = (g.M + BM - 1) / BM;
+    const long long blocks = (long long)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<T, TA, TB, BM, BN, WM, WN>), dim3((unsigned)blocks),
                        dim3(64 * WM * WN), 0, stream, g);
