@@ -66,8 +66,8 @@ struct SegV {
         : p0(static_cast<const T*>(s[0].p)), p1(static_cast<const T*>(s[1].p)),
           p2(static_cast<const T*>(s[2].p)), ld0(s[0].ld), ld1(s[1].ld), ld2(s[2].ld),
           st1(s[1].start), st2(s[2].start) {}
-    // Address of element (r, x) where x runs along the split dimension and r across it
-    // (selects, no branches: the loads that use it stay unconditional).
+    // Address of element (r, x) where x runs along the split dimension and r across it (every
+    // segment's address is formed and one is selected; the load that uses it is unconditional).
     __device__ inline const T* at(long long r, int x) const {
         const T* a0 = p0 + r * ld0 + x;
         const T* a1 = p1 + r * ld1 + (x - st1);
