@@ -400,10 +400,11 @@ hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream)
 // Heads per workgroup: the largest divisor G of g that is at most four.
 // * head_dim <= 64, bf16, few query blocks (B * Hq * T / 32 <= 2048, i.e. fewer than two
 //   waves per SIMD): one 32-row block per head (two for G <= 2) and two key splits.
-// * head_dim <= 64 otherwise: two waves per head (four when G <= 2), no key split; for bf16
-//   head_dim 64 each wave then owns 64 query rows (QB = 2) if 512+ workgroups remain.
+// * head_dim <= 64 otherwise: four waves per head when G <= 2 or (bf16) G = 3, else two; no
+//   key split; for bf16 head_dim 64 with 6 or 8 waves, each wave then owns 64 query rows
+//   (QB = 2) if 512+ workgroups remain.
 // * head_dim 128: one wave per head (4/G when G <= 2), no key split (LDS and registers).
-// Every shape gives 4, 6 or 8 waves (3 or 4 for head_dim 128).
+// Every shape gives 4, 6, 8 or 12 waves (3 or 4 for head_dim 128).
 template <typename T, int D>
 void pick_fwd_shape(const FwdArgs& a, int* G, int* WPH, int* KSPL) {
     const int g = a.Hq / a.Hkv;
@@ -422,7 +423,7 @@ void pick_fwd_shape(const FwdArgs& a, int* G, int* WPH, int* KSPL) {
         *WPH = (G_ <= 2) ? 2 : 1;
         *KSPL = 2;
     } else {
-        *WPH = (G_ <= 2) ? 4 : 2;
+        *WPH = (G_ <= 2 || (G_ == 3 && sizeof(T) == 2)) ? 4 : 2;
         *KSPL = 1;
     }
 }
@@ -447,7 +448,12 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
         }
         // Without a key split, bf16 head_dim-64 waves own two 32-row query blocks (QB = 2)
         // when that still leaves at least two workgroups per CU: every K / V fragment read
-        // from LDS then feeds two matrix-core instructions.
+        // from LDS then feeds two matrix-core instructions.  Three heads per workgroup take
+        // twelve 32-row waves instead (three per SIMD: six waves would leave two SIMDs with
+        // one wave each), which measured faster than six 64-row waves.
+        if constexpr (sizeof(T) == 2) {
+            if (nw == 12) return launch_fwd_cfg<T, D, QB, BN, 12, 1>(a, G, WPH, stream);
+        }
         if constexpr (sizeof(T) == 2 && D == 64) {
             const long long wgs = (long long)a.B * a.Hkv * ((a.Hq / a.Hkv) / G) *
                                   ((a.T + WPH * 64 - 1) / (WPH * 64));

@@ -173,3 +173,23 @@ def test_rope_qk_one_launch(dt):
     qo, ko = ea.rope_apply_qk(q, k, 10000.0)
     torch.cuda.synchronize()
     assert torch.equal(q2, qo) and torch.equal(k2, ko)
+
+
+@pytest.mark.parametrize("case", [(16, 512, 12, 4, 32), (4, 1500, 18, 3, 64), (2, 2100, 12, 4, 64)],
+                         ids=lambda c: "B%d_T%d_H%d-%d_D%d" % c)
+def test_forward_three_head_workgroups(case):
+    # bf16 problems with more than 2048 query blocks and three heads per K/V group take the
+    # 12-wave forward workgroups (four 32-row waves per head); g = 6 also groups three heads.
+    B, T, Hq, Hkv, D = case
+    seed = 7700 + T + D + Hq
+    say("[parity] forward, three heads per workgroup, %s seed %d" % (case, seed))
+    q = W.make_random((B, T, Hq, D), seed, "bf16").cuda()
+    k = W.make_random((B, T, Hkv, D), seed + 1, "bf16").cuda()
+    v = W.make_random((B, T, Hkv, D), seed + 2, "bf16").cuda()
+    o, lse = ea.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    b, kv = B - 1, Hkv - 1
+    g = Hq // Hkv
+    hs = slice(kv * g, (kv + 1) * g)
+    o_ref, lse_ref = oracle.attn_fwd(q[b:b + 1, :, hs], k[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1])
+    check_fwd("bf16", o[b:b + 1, :, hs], lse[b:b + 1, hs], o_ref, lse_ref, "fwd slice")
