@@ -708,6 +708,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
         dq_role<T, D, K::BNQ, NW>(a, smem, item, kvh, b);
 }
 
+// The dQ role alone, with only its own LDS; NW may exceed the dK/dV role's wave count.
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int BNQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+    using Dq = DqCfg<T, D, BNQ, NW>;
+    __shared__ __attribute__((aligned(16))) char smem[2 * (size_t)Dq::STAGE * sizeof(T)];
+    const int HB = a.B * a.Hkv;
+    const int m = blockIdx.x / HB;
+    const int rem = blockIdx.x % HB;
+    dq_role<T, D, BNQ, NW>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+}
+
 template <typename T, int D>
 hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, int seq, int Hq,
                         float* cs, const RopeArgs* rope, hipStream_t stream) {
@@ -801,15 +813,35 @@ hipError_t launch_bwd_cfg(const BwdArgs& a0, int G, int WPH, int roles, hipStrea
     return hipGetLastError();
 }
 
+template <typename T, int D, int NW>
+hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) {
+    BwdArgs a = a0;
+    a.G = G;
+    a.WPH = WPH;
+    a.nhc = (a.Hq / a.Hkv) / G;
+    a.ntq_dq = (a.T + WPH * 32 - 1) / (WPH * 32);
+    a.roles = 2;
+    a.norder = 0;
+    const long long blocks = (long long)a.ntq_dq * a.nhc * a.B * a.Hkv;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_dq_only(const BwdArgs& a, int G, int WPH, hipStream_t stream) {
-    const int nw = G * WPH;
     if constexpr (D >= 128) {
-        return launch_bwd_cfg<T, D, 4>(a, G, WPH, 2, stream);
+        return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
     } else {
-        if (nw == 6) return launch_bwd_cfg<T, D, 6>(a, G, WPH, 2, stream);
-        if (nw == 4) return launch_bwd_cfg<T, D, 4>(a, G, WPH, 2, stream);
-        return launch_bwd_cfg<T, D, 8>(a, G, WPH, 2, stream);
+        // Three heads: 12 waves (three per SIMD) instead of 6 (two SIMDs with one wave more
+        // than the others), when the launch still has two workgroups per CU.
+        if constexpr (sizeof(T) == 2)
+            if (G == 3 && (long long)((a.T + 127) / 128) * (a.Hq / a.Hkv / 3) * a.B * a.Hkv >= 512)
+                return launch_dq_cfg<T, D, 12>(a, G, 4, stream);
+        const int nw = G * WPH;
+        if (nw == 6) return launch_dq_cfg<T, D, 6>(a, G, WPH, stream);
+        if (nw == 4) return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
+        return launch_dq_cfg<T, D, 8>(a, G, WPH, stream);
     }
 }
 

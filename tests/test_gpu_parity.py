@@ -193,3 +193,32 @@ def test_forward_three_head_workgroups(case):
     hs = slice(kv * g, (kv + 1) * g)
     o_ref, lse_ref = oracle.attn_fwd(q[b:b + 1, :, hs], k[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1])
     check_fwd("bf16", o[b:b + 1, :, hs], lse[b:b + 1, hs], o_ref, lse_ref, "fwd slice")
+
+
+@pytest.mark.parametrize("case", [(16, 1100, 12, 4, 32), (8, 2100, 12, 4, 64), (6, 1500, 24, 4, 64)],
+                         ids=lambda c: "B%d_T%d_H%d-%d_D%d" % c)
+def test_backward_three_head_workgroups(case):
+    # bf16 problems whose dQ launch runs alone with at least 512 workgroups of 128 query rows
+    # and three heads per workgroup take the 12-wave dQ workgroups; g = 6 takes two of them
+    # per K/V head.  Ragged query tails in every case.
+    B, T, Hq, Hkv, D = case
+    seed = 7800 + T + D + Hq
+    say("[parity] backward, three heads per dQ workgroup, %s seed %d" % (case, seed))
+    q = W.make_random((B, T, Hq, D), seed, "bf16").cuda()
+    k = W.make_random((B, T, Hkv, D), seed + 1, "bf16").cuda()
+    v = W.make_random((B, T, Hkv, D), seed + 2, "bf16").cuda()
+    do = W.make_random((B, T, Hq, D), seed + 3, "bf16").cuda()
+    o, lse = ea.attn_fwd(q, k, v)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    g = Hq // Hkv
+    for b, kv in ((B - 1, Hkv - 1), (0, 1)):
+        hs = slice(kv * g, (kv + 1) * g)
+        sq, sk, sv, sdo = (q[b:b + 1, :, hs], k[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1],
+                           do[b:b + 1, :, hs])
+        dq_ref, dk_ref, dv_ref = oracle.attn_bwd(sq, sk, sv, sdo)
+        check_grads("bf16", {"dq": dq[b:b + 1, :, hs], "dk": dk[b:b + 1, :, kv:kv + 1],
+                             "dv": dv[b:b + 1, :, kv:kv + 1]},
+                    {"dq": dq_ref, "dk": dk_ref, "dv": dv_ref}, "bwd slice b=%d kv=%d" % (b, kv))
