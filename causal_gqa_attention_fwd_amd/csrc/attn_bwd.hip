@@ -333,8 +333,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         for (int it = 0; it < niter; ++it) iteration(it, sa);
     }
 
-    // Sum the dK/dV partials of the query blocks in LDS, last block first, then store from
-    // the waves of query block 0 (dK scaled by `scale`).  Fixed order: deterministic.
+    // Sum the dK/dV partials of the query blocks in LDS, last block first (fixed order:
+    // deterministic).  The waves of query block 0 then hold the totals; they write them back
+    // row-major per key half ([dK | dV][32 keys][D] floats, dK scaled by `scale`), and every
+    // thread stores 16-byte row segments, with the inverse RoPE of dK applied pair by pair.
     float* red = reinterpret_cast<float*>(smem);
     const size_t rbase = (size_t)kh * 2 * C::NDB * 16 * 64;
     for (int o = C::NQH - 1; o >= 0; --o) {
@@ -357,36 +359,57 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
                 }
         }
     }
-    if (qh != 0) return;
-    if (a.rope_cs != nullptr) {
-        // dK_raw = R(-phi) dK.  Pair (d, d+1) of a key sits in lanes (l, l ^ 1) of one register.
-        const float sgn = (l32 & 1) ? -1.0f : 1.0f;
-        const float2* tab = reinterpret_cast<const float2*>(a.rope_cs);
+    __syncthreads();  // every partial read
+    if (qh == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = min(j * BN + kh * 32 + acc_row(r, half), a.T - 1);
+        for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                const float x = dkacc[db][r];
-                const float y = __shfl_xor(x, 1, 64);
-                const float2 w = tab[(long long)key * (D / 2) + ((db * 32 + l32) >> 1)];
-                dkacc[db][r] = x * w.x + sgn * (y * w.y);
+            for (int r = 0; r < 16; ++r) {
+                const size_t at = rbase + (size_t)acc_row(r, half) * D + db * 32 + l32;
+                red[at] = dkacc[db][r] * a.scale;
+                red[at + 32 * D] = dvacc[db][r];
             }
-        }
     }
+    __syncthreads();
+    constexpr int CPRo = D / C::EPC;       // 16-byte output chunks per row
+    constexpr int NCHO = 2 * BN * CPRo;    // chunks of dK and dV
     T* __restrict__ dkp = static_cast<T*>(a.dk);
     T* __restrict__ dvp = static_cast<T*>(a.dv);
+    for (int c = tid; c < NCHO; c += C::NT) {
+        const int tsel = c / (BN * CPRo);
+        const int cc = c % (BN * CPRo);
+        const int kl = cc / CPRo, part = cc % CPRo;
+        const int key = j * BN + kl;
+        if (key >= a.T) continue;
+        const float* src = red + (size_t)(kl >> 5) * 2 * C::NDB * 1024 + (size_t)tsel * 32 * D +
+                           (size_t)(kl & 31) * D + part * C::EPC;
+        float x[C::EPC];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = j * BN + kh * 32 + acc_row(r, half);
-        if (key < a.T) {
-            const long long off = (((long long)b * a.T + key) * a.Hkv + kvh) * D + l32;
+        for (int e = 0; e < C::EPC; e += 4) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + e);
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                dkp[off + db * 32] = from_f32<T>(dkacc[db][r] * a.scale);
-                dvp[off + db * 32] = from_f32<T>(dvacc[db][r]);
+            for (int u = 0; u < 4; ++u) x[e + u] = v4[u];
+        }
+        if (tsel == 0 && a.rope_cs != nullptr) {
+            // dK_raw = R(-phi) dK on each pair (2p, 2p + 1) of the chunk.
+            const float* tab = a.rope_cs + ((long long)key * (D / 2) + part * (C::EPC / 2)) * 2;
+#pragma unroll
+            for (int e = 0; e < C::EPC; e += 4) {
+                const f32x4 w = *reinterpret_cast<const f32x4*>(tab + e);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const float x0 = x[e + 2 * u], x1 = x[e + 2 * u + 1];
+                    const float cs = w[2 * u], sn = w[2 * u + 1];
+                    x[e + 2 * u] = x0 * cs + x1 * sn;
+                    x[e + 2 * u + 1] = x1 * cs - x0 * sn;
+                }
             }
         }
+        Vec16<T> out;
+#pragma unroll
+        for (int e = 0; e < C::EPC; ++e) out.set(e, from_f32<T>(x[e]));
+        T* dst = (tsel == 0 ? dkp : dvp) + (((long long)b * a.T + key) * a.Hkv + kvh) * D + part * C::EPC;
+        st16(dst, out);
     }
 }
 
