@@ -194,9 +194,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
     const int niter = g * nq;
 
     // Staging of Q_i / dO_i (16-byte chunks, row-major), LSE and D: HBM -> registers -> LDS,
-    // through NSET register sets (two for bf16: each stage's loads then have two iterations to
-    // land; one for fp32, whose registers are already spent on wider fragments).
-    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    // through NSET register sets (two for bf16 up to head_dim 64: each stage's loads then have
+    // two iterations to land; one for fp32 and for head_dim 128, whose registers are already
+    // spent on wider fragments and accumulators).
+    constexpr int NSET = (sizeof(T) == 2 && D < 128) ? 2 : 1;
     struct Stg {
         Vec16<T> q[C::NCH], d[C::NCH];
         float l, t;
@@ -300,12 +301,18 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
     if (niter > 0) {
         fetch(sa, 0);
         commit(sa, 0);
-        if constexpr (NSET == 2) {
-            if (niter > 1) fetch(sb, 1);
-            if (niter > 2) fetch(sa, 2);
-        } else {
-            if (niter > 1) fetch(sa, 1);
-        }
+    }
+    // The K_j / V_j loads were issued before stage 0's, which the commit has waited for.
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        settle(kf[s]);
+        settle(vf[s]);
+    }
+    if constexpr (NSET == 2) {
+        if (niter > 1) fetch(sb, 1);
+        if (niter > 2) fetch(sa, 2);
+    } else {
+        if (niter > 1) fetch(sa, 1);
     }
     auto iteration = [&](int it, Stg& nxt) {
         __syncthreads();  // stage it&1 visible; stage (it+1)&1 free
@@ -497,8 +504,9 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     }
 
     // Staging of one K/V tile, row-major 16-byte chunks, through NSET register sets (two for
-    // bf16, so that each tile's loads have two iterations to land).
-    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    // bf16 up to head_dim 64, so that each tile's loads have two iterations to land; one for
+    // head_dim 128, which keeps the kernel within 256 registers).
+    constexpr int NSET = (sizeof(T) == 2 && D < 128) ? 2 : 1;
     struct Stg {
         Vec16<T> k[C::NCH], v[C::NCH];
     };
@@ -682,7 +690,7 @@ __device__ inline int dkdv_rank(int j, const Sched& s) {  // merged position of 
 template <typename T, int D, int NW>
 struct BwdKernelCfg {
     static constexpr int BM = 16 * NW;  // dK/dV role: 2 key halves x NW/2 query blocks
-    static constexpr int BNQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // dQ role key tile
+    static constexpr int BNQ = (D == 128) ? 32 : 64;  // dQ role key tile
     using Dk = DkdvCfg<T, D, BM>;
     using Dq = DqCfg<T, D, BNQ, NW>;
     static constexpr size_t DQ_BYTES = 2 * (size_t)Dq::STAGE * sizeof(T);
@@ -733,8 +741,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
 
 // The dQ role alone, with only its own LDS; NW may exceed the dK/dV role's wave count.
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
-    constexpr int BNQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+// bf16 head_dim 128 (32-key tiles, one staging register set) fits 256 registers: two
+// workgroups per CU, two waves per SIMD.
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int BNQ = (D == 128) ? 32 : 64;
     using Dq = DqCfg<T, D, BNQ, NW>;
     __shared__ __attribute__((aligned(16))) char smem[2 * (size_t)Dq::STAGE * sizeof(T)];
     const int HB = a.B * a.Hkv;

@@ -80,7 +80,9 @@ struct FwdCfg {
 };
 
 template <typename T, int D, int QB, int BN, int NW, int KSPL>
-__global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
+// bf16 head_dim 128 with four waves is held to 256 registers (one staging register set), so
+// that two workgroups share a CU and each SIMD runs two waves instead of one.
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 2 : 1) void attn_fwd_kernel(FwdArgs a) {
     using C = FwdCfg<T, D, QB, BN, NW, KSPL>;
     using M = Mfma<T>;
     using frag = typename M::frag;
@@ -143,9 +145,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(FwdArgs a) {
 
     // Staging of one step (KSPL consecutive K/V tiles): HBM -> registers (fetch) -> LDS
     // (commit), 16-byte chunks, consecutive lanes on consecutive chunks of a row, through NSET
-    // register sets (two for bf16 with 32-row waves, so that each step's loads have two steps
-    // to land; 64-row waves have no registers to spare).
-    constexpr int NSET = (sizeof(T) == 2 && QB == 1) ? 2 : 1;
+    // register sets (two for bf16 with 32-row waves up to head_dim 64, so that each step's
+    // loads have two steps to land; 64-row waves and head_dim 128 have no registers to spare).
+    constexpr int NSET = (sizeof(T) == 2 && QB == 1 && D < 128) ? 2 : 1;
     struct Stg {
         Vec16<T> k[C::NCH], v[C::NCH];
     };

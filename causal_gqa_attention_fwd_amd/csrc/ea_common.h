@@ -162,6 +162,15 @@ struct Vec16 {
     }
 };
 
+// Loads issued before a loop and first used inside it: the compiler's wait-count insertion
+// cannot tell, inside the loop, whether such a load is still in flight, so it waits for every
+// outstanding load (the loop's own prefetches included) at that first use, in every
+// iteration.  settle(x) consumes x once at the call site, so the wait happens there, once.
+template <typename T>
+__device__ inline void settle(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
 template <typename T>
 __device__ inline Vec16<T> ld16(const T* p) {
     Vec16<T> v;
