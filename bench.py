@@ -15,8 +15,10 @@ Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--extra NAMES]
                     [--decode NAMES] [--noncausal NAMES] [--proj NAMES]
 
-Besides the headline step, the line carries the other timed paths of the library: extra
-workloads of the same step ('extra'), attention against a KV cache ('decode'), the
+Besides the headline step, the line carries the other timed paths of the library: the same
+step on the other workloads ('extra': by default T = 8192, the head_dim-128 GQA shape, the
+GPU-pipeline layer in bf16 and fp32, and the tiny CPU model), attention against a KV cache
+('decode'), the
 attention without the causal mask ('noncausal') and the projections on either side of the
 attention, forward and backward ('projections').
 """
@@ -388,13 +390,27 @@ def cpu_baseline(w, W):
             "seconds_per_step": round(t, 3)}
 
 
+def time_extra(args, torch, ea, W) -> dict:
+    """The other workloads, each timed like the headline step (fewer steps)."""
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
+        steps = max(5, args.steps // 5)
+        we, _, mse, _, ke = time_workload(name, steps, max(2, args.warmup // 5), torch, ea, W)
+        tf = we.flops_total() / (mse * 1e-3) / 1e12
+        extra[name] = {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(mse, 4),
+                       "frac_of_peak": round(tf / PEAK_TFLOPS[we.dtype], 4), "steps": steps,
+                       "config": we.describe(),
+                       "kernel_us": {k: round(v, 2) for k, v in ke.items()}}
+    return extra
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="blog_t1024")
-    ap.add_argument("--extra", default="long_t8192",
+    ap.add_argument("--extra", default="long_t8192,gqa_t4096_d128,gpu_model_bf16,gpu_model_f32,tiny_cpu_model",
                     help="comma-separated extra workloads timed the same way (reported under 'extra')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", default="decode_b8_tk8192,decode_mtp4_b16_tk1024",
@@ -441,6 +457,8 @@ def main() -> int:
         # headline step) appear in a profile by themselves.
         want = set(x for x in args.only.split(",") if x)
         out = {"only": sorted(want)}
+        if "extra" in want:
+            out["extra"] = time_extra(args, torch, ea, W)
         if "decode" in want:
             out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                              for name in [x for x in args.decode.split(",") if x]}
@@ -483,15 +501,7 @@ def main() -> int:
         "roofline_attn_fwd": roofline_for(w, kern_us, "attn_fwd"),
         "roofline_attn_bwd_main": roofline_for(w, kern_us, "attn_bwd_main"),
     }
-    extra = {}
-    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
-        steps = max(5, args.steps // 5)
-        we, _, mse, _, ke = time_workload(name, steps, max(2, args.warmup // 5), torch, ea, W)
-        tf = we.flops_total() / (mse * 1e-3) / 1e12
-        extra[name] = {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(mse, 4),
-                       "frac_of_peak": round(tf / PEAK_TFLOPS[we.dtype], 4), "steps": steps,
-                       "kernel_us": {k: round(v, 2) for k, v in ke.items()}}
-    out["extra"] = extra
+    out["extra"] = time_extra(args, torch, ea, W)
     out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                      for name in [x for x in args.decode.split(",") if x]}
     out["projections"] = {name: time_projections(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
