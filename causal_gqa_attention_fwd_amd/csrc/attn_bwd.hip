@@ -879,15 +879,15 @@ hipError_t launch_dq_only(const BwdArgs& a, int G, int WPH, hipStream_t stream) 
 }
 
 // roles: 1 = dK/dV, 2 = dQ, 3 = both.  Both roles share one launch when the dK/dV role alone
-// would not fill the chip twice over (then each role's causal tail overlaps the other's
-// work); otherwise they run as two launches, each with its own workgroup shape.
+// has at most two workgroups per CU (then each role's causal tail overlaps the other's work);
+// otherwise they run as two launches, each with its own workgroup shape.
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     constexpr int NWK = dkdv_waves<T, D>();
     int G, WPH;
     pick_dq_shape<D>(a.Hq / a.Hkv, &G, &WPH);
     const long long dkdv_blocks = (long long)((a.T + 63) / 64) * a.B * a.Hkv;
-    const bool fuse = roles == 3 && G * WPH <= NWK && dkdv_blocks <= 256;
+    const bool fuse = roles == 3 && G * WPH <= NWK && dkdv_blocks <= 512;
     if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
     if (roles & 1) {
         hipError_t e = launch_bwd_cfg<T, D, NWK>(a, G, WPH, 1, stream);

@@ -222,3 +222,30 @@ def test_backward_three_head_workgroups(case):
         check_grads("bf16", {"dq": dq[b:b + 1, :, hs], "dk": dk[b:b + 1, :, kv:kv + 1],
                              "dv": dv[b:b + 1, :, kv:kv + 1]},
                     {"dq": dq_ref, "dk": dk_ref, "dv": dv_ref}, "bwd slice b=%d kv=%d" % (b, kv))
+
+
+@pytest.mark.parametrize("case", [(4, 2100, 12, 4, 64), (2, 2100, 16, 8, 64), (4, 2100, 4, 4, 32)],
+                         ids=lambda c: "B%d_T%d_H%d-%d_D%d" % c)
+def test_backward_separate_launches(case):
+    # bf16 problems with more than 512 dK/dV workgroups run the two backward roles as two
+    # launches; these take the dQ-only kernel with six (three heads x two), eight (two heads x
+    # four) and four (one head x four) 32-row waves.  Ragged tails in every case.
+    B, T, Hq, Hkv, D = case
+    seed = 7900 + T + D + Hq
+    say("[parity] backward as two launches, %s seed %d" % (case, seed))
+    q = W.make_random((B, T, Hq, D), seed, "bf16").cuda()
+    k = W.make_random((B, T, Hkv, D), seed + 1, "bf16").cuda()
+    v = W.make_random((B, T, Hkv, D), seed + 2, "bf16").cuda()
+    do = W.make_random((B, T, Hq, D), seed + 3, "bf16").cuda()
+    o, lse = ea.attn_fwd(q, k, v)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for b, kv in ((B - 1, Hkv - 1), (0, 0)):
+        hs = slice(kv * g, (kv + 1) * g)
+        sq, sk, sv, sdo = (q[b:b + 1, :, hs], k[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1],
+                           do[b:b + 1, :, hs])
+        dq_ref, dk_ref, dv_ref = oracle.attn_bwd(sq, sk, sv, sdo)
+        check_grads("bf16", {"dq": dq[b:b + 1, :, hs], "dk": dk[b:b + 1, :, kv:kv + 1],
+                             "dv": dv[b:b + 1, :, kv:kv + 1]},
+                    {"dq": dq_ref, "dk": dk_ref, "dv": dv_ref}, "bwd slice b=%d kv=%d" % (b, kv))
