@@ -21,7 +21,9 @@
 //    barriers: each wave is independent.
 //  * Each chunk leaves a partial (O_c, LSE_c) in the workspace; a second kernel merges the
 //    chunks exactly, LSE = log sum_c e^{LSE_c}, O = sum_c e^{LSE_c - LSE} O_c (or the first
-//    kernel writes O and LSE directly when there is one chunk).
+//    kernel writes O and LSE directly when there is one chunk).  Small caches (a few chunks)
+//    take one launch instead: one workgroup per row block, a wave per chunk, the same merge
+//    through LDS.
 #include <cmath>
 #include <type_traits>
 
@@ -60,29 +62,21 @@ struct DecCfg {
     static_assert(kKT * CPR % 64 == 0, "V tile staging");
 };
 
+// One wave: chunk sp of row block rb of K/V head kvh in batch b.  On return oacc holds the
+// chunk's output O_c (normalised by its own row sums; lane = row l32, registers = head_dim
+// as in the accumulator layout) and lse its LSE_c (natural log, -inf for a row that sees no
+// key of the chunk).  Vs: this wave's private V tile in LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArgs a) {
+__device__ __forceinline__ void decode_chunk(const DecArgs& a, T* Vs, int b, int kvh, int rb, int sp,
+                                             f32x16 (&oacc)[DecCfg<T, D>::NDB], float& lse) {
     using C = DecCfg<T, D>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
 
-    __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * kKT * C::VS];
-
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    const long long item = (long long)blockIdx.x * kWavesPerWG + w;
-    const long long nitems = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
-    if (item >= nitems) return;
-    const int sp = (int)(item % a.nsplit);
-    long long rest = item / a.nsplit;
-    const int rb = (int)(rest % a.nrb);
-    rest /= a.nrb;
-    const int kvh = (int)(rest % a.Hkv);
-    const int b = (int)(rest / a.Hkv);
-    T* Vs = Vsh + w * kKT * C::VS;
 
     const T* __restrict__ qp = static_cast<const T*>(a.q);
     const T* __restrict__ kp = static_cast<const T*>(a.k);
@@ -142,7 +136,6 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     };
 
     float mrun = -INFINITY, l = 0.0f;
-    f32x16 oacc[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[db] = zero_acc();
 
@@ -204,24 +197,131 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     // Row totals (the two lane halves hold different keys) and the chunk's result.
     const float lt = l + __shfl_xor(l, 32, 64);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const float lse = lt > 0.0f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
+    lse = lt > 0.0f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= inv;
+}
+
+// The split launch: one wave per (batch, K/V head, row block, chunk); with several chunks the
+// partials go to the workspace for decode_merge_kernel, with one chunk straight to O and LSE.
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArgs a) {
+    using C = DecCfg<T, D>;
+    __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * kKT * C::VS];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const long long item = (long long)blockIdx.x * kWavesPerWG + w;
+    const long long nitems = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
+    if (item >= nitems) return;
+    const int sp = (int)(item % a.nsplit);
+    long long rest = item / a.nsplit;
+    const int rb = (int)(rest % a.nrb);
+    rest /= a.nrb;
+    const int kvh = (int)(rest % a.Hkv);
+    const int b = (int)(rest / a.Hkv);
+
+    f32x16 oacc[C::NDB];
+    float lse;
+    decode_chunk<T, D>(a, Vsh + w * kKT * C::VS, b, kvh, rb, sp, oacc, lse);
+
+    const int r = rb * 32 + l32;
+    if (r >= a.R) return;  // padding rows; the merge reads real rows only
     if (a.nsplit == 1) {
-        if (!row_ok) return;
+        const int ti = r / a.g, head = kvh * a.g + r % a.g;
         T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) orow[db * 32 + acc_row(rr, half)] = from_f32<T>(oacc[db][rr] * inv);
+            for (int rr = 0; rr < 16; ++rr) orow[db * 32 + acc_row(rr, half)] = from_f32<T>(oacc[db][rr]);
         if (half == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = lse;
         return;
     }
-    if (!row_ok) return;  // the merge reads real rows only
     float* po = a.part_o + item * 32 * D + (long long)l32 * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) po[db * 32 + acc_row(rr, half)] = oacc[db][rr] * inv;
+        for (int rr = 0; rr < 16; ++rr) po[db * 32 + acc_row(rr, half)] = oacc[db][rr];
     if (half == 0) a.part_lse[item * 32 + l32] = lse;
+}
+
+// The single launch for caches of at most NW chunks: one workgroup per (batch, K/V head, row
+// block), wave w computing chunk w; the partials then meet in LDS (over the V tiles, after a
+// barrier) and are merged exactly as decode_merge_kernel does, chunks in order.
+// Waves of the single launch, sized so that each wave keeps the split launch's registers
+// (four waves per SIMD for bf16 head_dim 32, two for head_dim 64 and fp32 head_dim 32, one
+// for head_dim 128).
+template <typename T, int D>
+constexpr int fused_max_chunks() {
+    return D >= 128 ? 4 : (sizeof(T) == 2 && D <= 32) ? 16 : 8;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_kernel(DecArgs a) {
+    using C = DecCfg<T, D>;
+    constexpr int NW = fused_max_chunks<T, D>();
+    constexpr int PST = D + 1;  // row stride of a partial (odd: lanes of one column on distinct banks)
+    constexpr size_t V_BYTES = (size_t)NW * kKT * C::VS * sizeof(T);
+    constexpr size_t P_BYTES = (size_t)NW * 32 * PST * sizeof(float);
+    __shared__ __attribute__((aligned(16))) char smem[(V_BYTES > P_BYTES ? V_BYTES : P_BYTES) + NW * 32 * sizeof(float)];
+    float* part = reinterpret_cast<float*>(smem);
+    float* wts = reinterpret_cast<float*>(smem + (V_BYTES > P_BYTES ? V_BYTES : P_BYTES));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int ns = a.nsplit;  // == blockDim.x / 64
+    const int rb = blockIdx.x % a.nrb;
+    const int kvh = (blockIdx.x / a.nrb) % a.Hkv;
+    const int b = blockIdx.x / (a.nrb * a.Hkv);
+
+    f32x16 oacc[C::NDB];
+    float lse;
+    decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, oacc, lse);
+    __syncthreads();  // every wave is done with its V tile
+    {
+        float* po = part + (size_t)w * 32 * PST + l32 * PST;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) po[db * 32 + acc_row(rr, half)] = oacc[db][rr];
+        if (half == 0) wts[w * 32 + l32] = lse;
+    }
+    __syncthreads();
+    // Row weights e^{LSE_c - m} / sum (m: the row's largest LSE_c; chunk 0 holds key 0, which
+    // every row sees, so m is finite), and the row's LSE.
+    const int nrows = min(32, a.R - rb * 32);
+    if (tid < nrows) {
+        float m = -INFINITY;
+        for (int c = 0; c < ns; ++c) m = fmaxf(m, wts[c * 32 + tid]);
+        float z = 0.0f;
+        for (int c = 0; c < ns; ++c) {
+            const float ls = wts[c * 32 + tid];
+            const float wc = (ls == -INFINITY) ? 0.0f : expf(ls - m);
+            wts[c * 32 + tid] = wc;
+            z += wc;
+        }
+        const float iz = 1.0f / z;
+        for (int c = 0; c < ns; ++c) wts[c * 32 + tid] *= iz;
+        const int r = rb * 32 + tid;
+        const int ti = r / a.g, head = kvh * a.g + r % a.g;
+        a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
+    }
+    __syncthreads();
+    for (int e = tid; e < nrows * D; e += ns * 64) {
+        const int rl = e / D, d = e % D;
+        float acc = 0.0f;
+        for (int c = 0; c < ns; ++c) acc += wts[c * 32 + rl] * part[((size_t)c * 32 + rl) * PST + d];
+        const int r = rb * 32 + rl;
+        const int ti = r / a.g, head = kvh * a.g + r % a.g;
+        static_cast<T*>(a.o)[(((long long)b * a.Tq + ti) * a.Hq + head) * D + d] = from_f32<T>(acc);
+    }
 }
 
 // Merge of the chunks: one wave per row.  The lanes first take the chunks' LSE values (max,
@@ -300,6 +400,20 @@ DecPlan plan_decode(int B, int Tq, int Tk, int Hq, int Hkv) {
 
 template <typename T, int D>
 hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
+    // Caches split into at most twice as many chunks as the single launch has waves take the
+    // single launch, with fewer, longer chunks: the second launch and the workspace round trip
+    // cost more there than the waves the split would add.
+    constexpr int F = fused_max_chunks<T, D>();
+    if (a.nsplit > 1 && a.nsplit <= 2 * F) {
+        const int tiles = (a.Tk + kKT - 1) / kKT;
+        const int ns = a.nsplit < F ? a.nsplit : F;
+        a.chunk = ((tiles + ns - 1) / ns) * kKT;
+        a.nsplit = (a.Tk + a.chunk - 1) / a.chunk;
+        const long long blocks = (long long)a.B * a.Hkv * a.nrb;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_fused_kernel<T, D>), dim3((unsigned)blocks), dim3(64 * a.nsplit), 0, stream, a);
+        return hipGetLastError();
+    }
     const long long items = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
     const long long blocks = (items + kWavesPerWG - 1) / kWavesPerWG;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
