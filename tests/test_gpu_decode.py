@@ -3,8 +3,8 @@ attn_fwd_kv on the same seeded inputs, through the C ABI.
 
 Cases cover one and several new tokens, caches that fit one chunk (no merge), caches split
 over a few chunks (one launch, merged in LDS: B2_Tq2_Tk100, B1_Tq4_Tk129, B1_Tq16_Tk777,
-B1_Tq11_Tk300) and over many (merge launch), ragged cache lengths, every head_dim, both
-dtypes and several head groupings; the cache shape of a 32/8-head, head_dim-128 model at
+B2_Tq5_Tk2049, B1_Tq11_Tk300) and over many (merge launch: B3_Tq1_Tk1000, B4_Tq1_Tk4097),
+ragged cache lengths, every head_dim, both dtypes and several head groupings; the cache shape of a 32/8-head, head_dim-128 model at
 8192 cached positions is run at full size.  With Tq = Tk the result must match attn_fwd.
 """
 import numpy as np
