@@ -76,7 +76,7 @@ struct FwdCfg {
     static constexpr int NBUF = 2 * KSPL;     // double buffer per key split
     // Merge area for the key splits' partials (reuses the K tiles after the loop).
     static constexpr int MERGE_FLOATS = (NW / KSPL) * (16 * (D / 32) * QB + 2 * QB) * 64;
-    static_assert(KSPL == 1 || MERGE_FLOATS * 4 <= (int)(NBUF * KBUF * sizeof(T)), "merge area");
+    static_assert(KSPL == 1 || MERGE_FLOATS * 4 <= (int)(2 * NBUF * KBUF * sizeof(T)), "merge area");
 };
 
 template <typename T, int D, int QB, int BN, int NW, int KSPL>
@@ -88,8 +88,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
 
-    __shared__ __attribute__((aligned(16))) T Ks[C::NBUF * C::KBUF];
-    __shared__ __attribute__((aligned(16))) T Vs[C::NBUF * C::KBUF];
+    // K tiles, then V tiles (one array: the key-split merge reuses both).
+    __shared__ __attribute__((aligned(16))) T KVs[2 * C::NBUF * C::KBUF];
+    T* const Ks = KVs;
+    T* const Vs = KVs + C::NBUF * C::KBUF;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -146,8 +148,9 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     // Staging of one step (KSPL consecutive K/V tiles): HBM -> registers (fetch) -> LDS
     // (commit), 16-byte chunks, consecutive lanes on consecutive chunks of a row, through NSET
     // register sets (two for bf16 with 32-row waves up to head_dim 64, so that each step's
-    // loads have two steps to land; 64-row waves and head_dim 128 have no registers to spare).
-    constexpr int NSET = (sizeof(T) == 2 && QB == 1 && D < 128) ? 2 : 1;
+    // loads have two steps to land; 64-row waves, head_dim 128 and the twelve-wave key split,
+    // held to 168 registers, have none to spare).
+    constexpr int NSET = (sizeof(T) == 2 && QB == 1 && D < 128 && !(KSPL == 2 && NW == 12)) ? 2 : 1;
     struct Stg {
         Vec16<T> k[C::NCH], v[C::NCH];
     };
@@ -401,7 +404,8 @@ hipError_t launch_fwd_cfg(const FwdArgs& a0, int G, int WPH, hipStream_t stream)
 
 // Heads per workgroup: the largest divisor G of g that is at most four.
 // * head_dim <= 64, bf16, few query blocks (B * Hq * T / 32 <= 2048, i.e. fewer than two
-//   waves per SIMD): one 32-row block per head (two for G <= 2) and two key splits.
+//   waves per SIMD): two 32-row blocks per head (one for G = 4) and two key splits, so that
+//   three heads make twelve waves, three per SIMD.
 // * head_dim <= 64 otherwise: four waves per head when G <= 2 or (bf16) G = 3, else two; no
 //   key split; for bf16 head_dim 64 with 6 or 8 waves, each wave then owns 64 query rows
 //   (QB = 2) if 512+ workgroups remain.
@@ -422,7 +426,7 @@ void pick_fwd_shape(const FwdArgs& a, int* G, int* WPH, int* KSPL) {
         *WPH = (G_ >= 3) ? 1 : 4 / G_;
         *KSPL = 1;
     } else if (sizeof(T) == 2 && qblocks <= 2048) {
-        *WPH = (G_ <= 2) ? 2 : 1;
+        *WPH = (G_ <= 3) ? 2 : 1;
         *KSPL = 2;
     } else {
         *WPH = (G_ <= 2 || (G_ == 3 && sizeof(T) == 2)) ? 4 : 2;
@@ -443,6 +447,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     } else {
         if constexpr (sizeof(T) == 2) {
             if (KSPL == 2) {
+                if (nw == 12) return launch_fwd_cfg<T, D, QB, BN, 12, 2>(a, G, WPH, stream);
                 if (nw == 6) return launch_fwd_cfg<T, D, QB, BN, 6, 2>(a, G, WPH, stream);
                 if (nw == 4) return launch_fwd_cfg<T, D, QB, BN, 4, 2>(a, G, WPH, stream);
                 return launch_fwd_cfg<T, D, QB, BN, 8, 2>(a, G, WPH, stream);

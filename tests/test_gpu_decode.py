@@ -36,7 +36,9 @@ def test_decode_parity(case):
     k = W.make_random((B, Tk, Hkv, D), seed + 1, dt).cuda()
     v = W.make_random((B, Tk, Hkv, D), seed + 2, dt).cuda()
     o, lse = ea.attn_decode(q, k, v)
+    o2, lse2 = ea.attn_decode(q, k, v)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)  # chunks merged in a fixed order
     o_ref, lse_ref = oracle.attn_fwd_kv(q, k, v)
     check_fwd(dt, o, lse, o_ref, lse_ref, "decode")
 
