@@ -316,11 +316,21 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
         for (int st = 0; st < nsteps; ++st) step(st, sa);
     }
 
+    // Output staging region of this wave (16 rows of O at a time, row stride OS): the merge
+    // slot of the key-split path, else a slice of the K/V area once every wave is done with it.
+    constexpr int OS = D + C::EPC;
+    T* ostage;
+    if constexpr (KSPL == 1) {
+        __syncthreads();  // every wave is done with the K/V tiles
+        ostage = Ks + (size_t)w * 16 * OS;
+    }
+
     if constexpr (KSPL == 2) {
         // Merge the two key splits: m = max(m0, m1), a_i = 2^(m_i - m),
         // l = a0 l0 + a1 l1, O = a0 O0 + a1 O1 (per lane, before the halves combine).
         constexpr int PER = 16 * C::NDB * QB + 2 * QB;
         float* mb = reinterpret_cast<float*>(Ks) + (size_t)slot * PER * 64;
+        ostage = reinterpret_cast<T*>(mb);
         __syncthreads();  // every wave is done with the K/V tiles
         if (ks == 1 && active) {
 #pragma unroll
@@ -355,33 +365,54 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     }
 
     if (!active) return;
+    // O leaves through LDS: the lanes of 16 rows write their row (normalised, in the I/O
+    // dtype) to the staging region, then the wave stores whole 16-byte row segments, eight
+    // lanes per 128-byte row (the accumulator layout alone would give 8-byte pieces).
     T* __restrict__ op = static_cast<T*>(a.o);
+    constexpr int CPRo = D / C::EPC;
+    auto wave_sync = [&]() {  // this wave's LDS accesses before / after, in order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int tq = q0 + qb * 32 + l32;
         const float lt = l[qb] + xor_shfl32(l[qb]);
-        if (tq < a.T) {
-            const float inv = 1.0f / lt;
-            T* orow = op + (((long long)b * a.T + tq) * a.Hq + head) * D;
+        const float inv = 1.0f / lt;
+        if (half == 0 && tq < a.T)
+            a.lse[((long long)b * a.Hq + head) * a.T + tq] = (mrun[qb] + __log2f(lt)) * kLn2;
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
+        for (int hr = 0; hr < 2; ++hr) {
+            wave_sync();  // the previous round's reads (or the merge's) are done
+            if ((l32 >> 4) == hr) {
+                T* srow = ostage + (l32 & 15) * OS;
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const int d0 = db * 32 + 8 * a4 + 4 * half;
-                    if constexpr (sizeof(T) == 2) {
-                        bf16x4 v;
+                for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[qb][db][4 * a4 + e] * inv);
-                        *reinterpret_cast<bf16x4*>(orow + d0) = v;
-                    } else {
-                        f32x4 v;
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const int d0 = db * 32 + 8 * a4 + 4 * half;
+                        if constexpr (sizeof(T) == 2) {
+                            bf16x4 v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = oacc[qb][db][4 * a4 + e] * inv;
-                        *reinterpret_cast<f32x4*>(orow + d0) = v;
+                            for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[qb][db][4 * a4 + e] * inv);
+                            *reinterpret_cast<bf16x4*>(srow + d0) = v;
+                        } else {
+                            f32x4 v;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = oacc[qb][db][4 * a4 + e] * inv;
+                            *reinterpret_cast<f32x4*>(srow + d0) = v;
+                        }
                     }
-                }
             }
-            if (half == 0) a.lse[((long long)b * a.Hq + head) * a.T + tq] = (mrun[qb] + __log2f(lt)) * kLn2;
+            wave_sync();
+            for (int c = lane; c < 16 * CPRo; c += 64) {
+                const int row = c / CPRo, part = c % CPRo;
+                const int t = q0 + qb * 32 + hr * 16 + row;
+                if (t < a.T)
+                    st16(op + (((long long)b * a.T + t) * a.Hq + head) * D + part * C::EPC,
+                         ld16(ostage + row * OS + part * C::EPC));
+            }
         }
     }
 }
