@@ -600,6 +600,9 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     // s - 1; the set is then refilled with tile s + NSET.
     fetch(sa, 0);
     commit(sa, 0);
+    // The LSE / D loads were issued before tile 0's, which the commit has waited for.
+    settle(lse2);
+    settle(dtv);
     if constexpr (NSET == 2) {
         if (jmax >= 1) fetch(sb, 1);
         if (jmax >= 2) fetch(sa, 2);
@@ -742,9 +745,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
 // The dQ role alone, with only its own LDS; NW may exceed the dK/dV role's wave count.
 template <typename T, int D, int NW>
 // bf16 head_dim 128 (32-key tiles, one staging register set) fits 256 registers: two
-// workgroups per CU, two waves per SIMD.
+// workgroups per CU, two waves per SIMD.  Twelve waves (three per SIMD, 168 registers) take
+// 32-key tiles too: with 64-key tiles the kernel spills.
 __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
-    constexpr int BNQ = (D == 128) ? 32 : 64;
+    constexpr int BNQ = (D == 128 || NW == 12) ? 32 : 64;
     using Dq = DqCfg<T, D, BNQ, NW>;
     __shared__ __attribute__((aligned(16))) char smem[2 * (size_t)Dq::STAGE * sizeof(T)];
     const int HB = a.B * a.Hkv;
