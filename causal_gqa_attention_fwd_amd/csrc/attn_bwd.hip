@@ -111,12 +111,13 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------------------
 // 2. dK, dV: KV-stationary.
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, int BM>
+template <typename T, int D, int BM, int QB = 1>
 struct DkdvCfg {
     static constexpr int KPL = Mfma<T>::KPL;
     static constexpr int BN = 64;               // keys per workgroup
     static constexpr int NKH = BN / 32;         // key halves
-    static constexpr int NQH = BM / 32;         // query blocks per iteration
+    static constexpr int QW = 32 * QB;          // query rows of a wave per iteration
+    static constexpr int NQH = BM / QW;         // query blocks per iteration
     static constexpr int NW = NKH * NQH;
     static constexpr int NT = 64 * NW;
     static constexpr int NS = D / (2 * KPL);    // MFMA steps over head_dim
@@ -139,10 +140,12 @@ struct DkdvCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.
-template <typename T, int D, int BM>
+// One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.  Each wave takes
+// 32 keys and QB blocks of 32 query rows per iteration; with QB = 2 the two blocks' products
+// and exponentials are independent chains that the scheduler interleaves.
+template <typename T, int D, int BM, int QB = 1>
 __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, int kvh, int b) {
-    using C = DkdvCfg<T, D, BM>;
+    using C = DkdvCfg<T, D, BM, QB>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
@@ -197,7 +200,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
     // through NSET register sets (two for bf16 up to head_dim 64: each stage's loads then have
     // two iterations to land; one for fp32 and for head_dim 128, whose registers are already
     // spent on wider fragments and accumulators).
-    constexpr int NSET = (sizeof(T) == 2 && D < 128) ? 2 : 1;
+    constexpr int NSET = (sizeof(T) == 2 && D < 128 && QB == 1) ? 2 : 1;
     struct Stg {
         Vec16<T> q[C::NCH], d[C::NCH];
         float l, t;
@@ -258,40 +261,55 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         const T* dOs = reinterpret_cast<const T*>(base + C::OFF_DO);
         const float* lse2s = reinterpret_cast<const float*>(base + C::OFF_LSE);
         const float* dts = reinterpret_cast<const float*>(base + C::OFF_DT);
-        // S = Q K^T and dP = dO V^T on this wave's 32 x 32 block (lanes = keys).
-        f32x16 sacc = zero_acc(), dpacc = zero_acc();
+        // S = Q K^T and dP = dO V^T on this wave's QB 32 x 32 blocks (lanes = keys).
+        f32x16 sacc[QB], dpacc[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            sacc[qb] = zero_acc();
+            dpacc[qb] = zero_acc();
+        }
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
-            const int ro = (qh * 32 + l32) * C::QS + half * (D / 2) + s * KPL;
-            sacc = M::mma(load_frag<T>(&Qs[ro]), kf[s], sacc);
-            dpacc = M::mma(load_frag<T>(&dOs[ro]), vf[s], dpacc);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int ro = (qh * C::QW + qb * 32 + l32) * C::QS + half * (D / 2) + s * KPL;
+                sacc[qb] = M::mma(load_frag<T>(&Qs[ro]), kf[s], sacc[qb]);
+                dpacc[qb] = M::mma(load_frag<T>(&dOs[ro]), vf[s], dpacc[qb]);
+            }
         }
         // P = exp(S - LSE) (masked where key > query); dS = P (dP - D).
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int lq0 = qh * 32 + 8 * r4 + 4 * half;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[lq0]);
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int r = 4 * r4 + c;
-                float p = __builtin_amdgcn_exp2f(sacc[r] * a.sl2 - l4[c]);
-                if constexpr (MASK) {
-                    if (mykey > i * BM + lq0 + c) p = 0.0f;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int lq0 = qh * C::QW + qb * 32 + 8 * r4 + 4 * half;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[lq0]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * r4 + c;
+                    float p = __builtin_amdgcn_exp2f(sacc[qb][r] * a.sl2 - l4[c]);
+                    if constexpr (MASK) {
+                        if (mykey > i * BM + lq0 + c) p = 0.0f;
+                    }
+                    sacc[qb][r] = p;
+                    dpacc[qb][r] = p * (dpacc[qb][r] - d4[c]);
                 }
-                sacc[r] = p;
-                dpacc[r] = p * (dpacc[r] - d4[c]);
             }
         }
-        // dV += P^T dO and dK += dS^T Q (contraction over this wave's 32 queries).
+        // dV += P^T dO and dK += dS^T Q (contraction over this wave's queries).
 #pragma unroll
-        for (int ps = 0; ps < C::PS; ++ps) {
-            const frag pf = acc_to_frag<T>(sacc, ps * KPL);
-            const frag dsf = acc_to_frag<T>(dpacc, ps * KPL);
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                dvacc[db] = M::mma(pf, load_rows_frag<T>(dOs, C::QS, qh * 32, ps, db * 32), dvacc[db]);
-                dkacc[db] = M::mma(dsf, load_rows_frag<T>(Qs, C::QS, qh * 32, ps, db * 32), dkacc[db]);
+            for (int ps = 0; ps < C::PS; ++ps) {
+                const frag pf = acc_to_frag<T>(sacc[qb], ps * KPL);
+                const frag dsf = acc_to_frag<T>(dpacc[qb], ps * KPL);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    const int r0 = qh * C::QW + qb * 32;
+                    dvacc[db] = M::mma(pf, load_rows_frag<T>(dOs, C::QS, r0, ps, db * 32), dvacc[db]);
+                    dkacc[db] = M::mma(dsf, load_rows_frag<T>(Qs, C::QS, r0, ps, db * 32), dkacc[db]);
+                }
             }
         }
     };
@@ -324,8 +342,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         // Skip blocks whose keys all follow their queries; mask blocks crossing the diagonal.
         // Without the causal mask nothing is masked: keys past the end have K = V = 0 and
         // their dK / dV are never stored; queries past the end have P = 0 (LSE = +inf).
-        const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * 32;
-        if (a.causal && kfirst > qfirst + 31) return;
+        const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * C::QW;
+        if (a.causal && kfirst > qfirst + C::QW - 1) return;
         if (a.causal && kfirst + 31 > qfirst)
             compute(it, it & 1, std::true_type{});
         else
@@ -757,6 +775,20 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void
     dq_role<T, D, BNQ, NW>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
+// The dK/dV role in a launch of its own, bf16 up to head_dim 64: four waves of 32 keys x 64
+// query rows over 128-row stages; two workgroups (eight waves) per CU, each with its own
+// barriers.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+    using Dk = DkdvCfg<T, D, 128, 2>;
+    static_assert(Dk::NW == 4, "four waves");
+    __shared__ __attribute__((aligned(16))) char smem[Dk::BYTES];
+    const int HB = a.B * a.Hkv;
+    const int m = blockIdx.x / HB;
+    const int rem = blockIdx.x % HB;
+    dkdv_role<T, D, 128, 2>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+}
+
 template <typename T, int D>
 hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, int seq, int Hq,
                         float* cs, const RopeArgs* rope, hipStream_t stream) {
@@ -866,6 +898,19 @@ hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) 
 }
 
 template <typename T, int D>
+hipError_t launch_dkdv_only(const BwdArgs& a0, hipStream_t stream) {
+    BwdArgs a = a0;
+    a.ntk = (a.T + 63) / 64;
+    a.ntq = (a.T + 127) / 128;
+    a.roles = 1;
+    a.norder = 0;
+    const long long blocks = (long long)a.ntk * a.B * a.Hkv;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
 hipError_t launch_dq_only(const BwdArgs& a, int G, int WPH, hipStream_t stream) {
     if constexpr (D >= 128) {
         return launch_dq_cfg<T, D, 4>(a, G, WPH, stream);
@@ -891,10 +936,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     int G, WPH;
     pick_dq_shape<D>(a.Hq / a.Hkv, &G, &WPH);
     const long long dkdv_blocks = (long long)((a.T + 63) / 64) * a.B * a.Hkv;
-    const bool fuse = roles == 3 && G * WPH <= NWK && dkdv_blocks <= 512;
+    const bool small = dkdv_blocks <= 512;
+    const bool fuse = roles == 3 && G * WPH <= NWK && small;
     if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
     if (roles & 1) {
-        hipError_t e = launch_bwd_cfg<T, D, NWK>(a, G, WPH, 1, stream);
+        // The four-wave dK/dV kernel pays once the launch has more than two workgroups per CU;
+        // below that the eight-wave role of the shared launch is used, so that the dK/dV entry
+        // point and the shared launch give bitwise the same dK and dV.
+        hipError_t e;
+        if constexpr (sizeof(T) == 2 && D <= 64) {
+            if (!small)
+                e = launch_dkdv_only<T, D>(a, stream);
+            else
+                e = launch_bwd_cfg<T, D, NWK>(a, G, WPH, 1, stream);
+        } else {
+            e = launch_bwd_cfg<T, D, NWK>(a, G, WPH, 1, stream);
+        }
         if (e != hipSuccess) return e;
     }
     if (roles & 2) return launch_dq_only<T, D>(a, G, WPH, stream);

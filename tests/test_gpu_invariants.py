@@ -136,10 +136,15 @@ def test_long_context_properties():
     assert lse[b, h, -1].item() >= s_last.max().item() - 1e-3
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_backward_stages_compose(dt):
-    B, T, Hq, Hkv, D = 2, 190, 8, 2, 64
-    say("[inv] backward stages dt=%s" % dt)
+@pytest.mark.parametrize("dt,shape", [("f32", (2, 190, 8, 2, 64)), ("bf16", (2, 190, 8, 2, 64)),
+                                      ("bf16", (4, 2100, 12, 4, 64)), ("bf16", (4, 2100, 4, 4, 32))],
+                         ids=["f32-small", "bf16-small", "bf16-T2100-D64", "bf16-T2100-D32"])
+def test_backward_stages_compose(dt, shape):
+    # Small problems run both roles in one launch, the T=2100 ones (more than 512 dK/dV
+    # workgroups) as two launches with the four-wave dK/dV kernel: either way the stage entry
+    # points must reproduce the one-call backward bitwise.
+    B, T, Hq, Hkv, D = shape
+    say("[inv] backward stages dt=%s shape=%s" % (dt, shape))
     q, k, v = rnd((B, T, Hq, D), 20, dt), rnd((B, T, Hkv, D), 21, dt), rnd((B, T, Hkv, D), 22, dt)
     do = rnd((B, T, Hq, D), 23, dt)
     o, lse = ea.attn_fwd(q, k, v)
