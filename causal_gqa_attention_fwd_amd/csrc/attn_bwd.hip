@@ -111,11 +111,11 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------------------
 // 2. dK, dV: KV-stationary.
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, int BM, int QB = 1>
+template <typename T, int D, int BM, int QB = 1, int BN_ = 64>
 struct DkdvCfg {
     static constexpr int KPL = Mfma<T>::KPL;
-    static constexpr int BN = 64;               // keys per workgroup
-    static constexpr int NKH = BN / 32;         // key halves
+    static constexpr int BN = BN_;              // keys per workgroup
+    static constexpr int NKH = BN / 32;         // 32-key blocks
     static constexpr int QW = 32 * QB;          // query rows of a wave per iteration
     static constexpr int NQH = BM / QW;         // query blocks per iteration
     static constexpr int NW = NKH * NQH;
@@ -143,9 +143,9 @@ struct DkdvCfg {
 // One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.  Each wave takes
 // 32 keys and QB blocks of 32 query rows per iteration; with QB = 2 the two blocks' products
 // and exponentials are independent chains that the scheduler interleaves.
-template <typename T, int D, int BM, int QB = 1>
+template <typename T, int D, int BM, int QB = 1, int BN_ = 64>
 __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, int kvh, int b) {
-    using C = DkdvCfg<T, D, BM, QB>;
+    using C = DkdvCfg<T, D, BM, QB, BN_>;
     using M = Mfma<T>;
     using frag = typename M::frag;
     constexpr int KPL = C::KPL;
@@ -775,18 +775,21 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void
     dq_role<T, D, BNQ, NW>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
-// The dK/dV role in a launch of its own, bf16 up to head_dim 64: four waves of 32 keys x 64
-// query rows over 128-row stages; two workgroups (eight waves) per CU, each with its own
-// barriers.
+// The dK/dV role in a launch of its own, bf16 up to head_dim 64: 128 keys per workgroup, as
+// eight waves of 32 keys x 64 query rows over 128-row stages.  Each staged Q / dO tile then
+// feeds twice as many keys as in the shared launch's 64-key workgroups, which halves the
+// load traffic per product; two query blocks per wave give the scheduler two independent
+// chains.
+constexpr int kDkdvBN = 128;
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
-    using Dk = DkdvCfg<T, D, 128, 2>;
-    static_assert(Dk::NW == 4, "four waves");
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+    using Dk = DkdvCfg<T, D, 128, 2, kDkdvBN>;
+    static_assert(Dk::NW == 8, "eight waves");
     __shared__ __attribute__((aligned(16))) char smem[Dk::BYTES];
     const int HB = a.B * a.Hkv;
     const int m = blockIdx.x / HB;
     const int rem = blockIdx.x % HB;
-    dkdv_role<T, D, 128, 2>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+    dkdv_role<T, D, 128, 2, kDkdvBN>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
 template <typename T, int D>
@@ -900,13 +903,13 @@ hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) 
 template <typename T, int D>
 hipError_t launch_dkdv_only(const BwdArgs& a0, hipStream_t stream) {
     BwdArgs a = a0;
-    a.ntk = (a.T + 63) / 64;
+    a.ntk = (a.T + kDkdvBN - 1) / kDkdvBN;
     a.ntq = (a.T + 127) / 128;
     a.roles = 1;
     a.norder = 0;
     const long long blocks = (long long)a.ntk * a.B * a.Hkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -940,9 +943,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     const bool fuse = roles == 3 && G * WPH <= NWK && small;
     if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
     if (roles & 1) {
-        // The four-wave dK/dV kernel pays once the launch has more than two workgroups per CU;
-        // below that the eight-wave role of the shared launch is used, so that the dK/dV entry
-        // point and the shared launch give bitwise the same dK and dV.
+        // The 128-key dK/dV kernel pays once the 64-key launch would have more than two
+        // workgroups per CU; below that the eight-wave role of the shared launch is used, so
+        // that the dK/dV entry point and the shared launch give bitwise the same dK and dV.
         hipError_t e;
         if constexpr (sizeof(T) == 2 && D <= 64) {
             if (!small)
