@@ -775,21 +775,25 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void
     dq_role<T, D, BNQ, NW>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
-// The dK/dV role in a launch of its own, bf16 up to head_dim 64: 128 keys per workgroup, as
-// eight waves of 32 keys x 64 query rows over 128-row stages.  Each staged Q / dO tile then
-// feeds twice as many keys as in the shared launch's 64-key workgroups, which halves the
-// load traffic per product; two query blocks per wave give the scheduler two independent
-// chains.
-constexpr int kDkdvBN = 128;
+// The dK/dV role in a launch of its own (bf16, large problems): waves of 32 keys x two 32-row
+// query blocks (two independent chains for the scheduler) over 128-row stages.  Up to head_dim
+// 64 a workgroup takes 128 keys as eight waves, so each staged Q / dO tile feeds twice as many
+// keys as in the shared launch's 64-key workgroups (half the load traffic per product); head
+// dim 128 takes 64 keys as four waves (460 registers: one wave per SIMD, 139 KB of LDS).
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
-    using Dk = DkdvCfg<T, D, 128, 2, kDkdvBN>;
-    static_assert(Dk::NW == 8, "eight waves");
-    __shared__ __attribute__((aligned(16))) char smem[Dk::BYTES];
+struct DkdvSolo {
+    static constexpr int BN = D <= 64 ? 128 : 64;
+    using Cfg = DkdvCfg<T, D, 128, 2, BN>;
+    static constexpr int NT = 64 * Cfg::NW;
+};
+template <typename T, int D>
+__global__ __launch_bounds__((DkdvSolo<T, D>::NT), 1) void bwd_dkdv_kernel(BwdArgs a) {
+    using S = DkdvSolo<T, D>;
+    __shared__ __attribute__((aligned(16))) char smem[S::Cfg::BYTES];
     const int HB = a.B * a.Hkv;
     const int m = blockIdx.x / HB;
     const int rem = blockIdx.x % HB;
-    dkdv_role<T, D, 128, 2, kDkdvBN>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+    dkdv_role<T, D, 128, 2, S::BN>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
 template <typename T, int D>
@@ -902,14 +906,15 @@ hipError_t launch_dq_cfg(const BwdArgs& a0, int G, int WPH, hipStream_t stream) 
 
 template <typename T, int D>
 hipError_t launch_dkdv_only(const BwdArgs& a0, hipStream_t stream) {
+    using S = DkdvSolo<T, D>;
     BwdArgs a = a0;
-    a.ntk = (a.T + kDkdvBN - 1) / kDkdvBN;
+    a.ntk = (a.T + S::BN - 1) / S::BN;
     a.ntq = (a.T + 127) / 128;
     a.roles = 1;
     a.norder = 0;
     const long long blocks = (long long)a.ntk * a.B * a.Hkv;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3((unsigned)blocks), dim3(S::NT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -943,11 +948,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     const bool fuse = roles == 3 && G * WPH <= NWK && small;
     if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
     if (roles & 1) {
-        // The 128-key dK/dV kernel pays once the 64-key launch would have more than two
-        // workgroups per CU; below that the eight-wave role of the shared launch is used, so
-        // that the dK/dV entry point and the shared launch give bitwise the same dK and dV.
+        // The separate dK/dV kernel pays once the 64-key launch would have more than two
+        // workgroups per CU; below that the role of the shared launch is used, so that the
+        // dK/dV entry point and the shared launch give bitwise the same dK and dV.
         hipError_t e;
-        if constexpr (sizeof(T) == 2 && D <= 64) {
+        if constexpr (sizeof(T) == 2) {
             if (!small)
                 e = launch_dkdv_only<T, D>(a, stream);
             else

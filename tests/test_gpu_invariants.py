@@ -137,11 +137,12 @@ def test_long_context_properties():
 
 
 @pytest.mark.parametrize("dt,shape", [("f32", (2, 190, 8, 2, 64)), ("bf16", (2, 190, 8, 2, 64)),
-                                      ("bf16", (4, 2100, 12, 4, 64)), ("bf16", (4, 2100, 4, 4, 32))],
-                         ids=["f32-small", "bf16-small", "bf16-T2100-D64", "bf16-T2100-D32"])
+                                      ("bf16", (4, 2100, 12, 4, 64)), ("bf16", (4, 2100, 4, 4, 32)),
+                                      ("bf16", (2, 2100, 16, 8, 128))],
+                         ids=["f32-small", "bf16-small", "bf16-T2100-D64", "bf16-T2100-D32", "bf16-T2100-D128"])
 def test_backward_stages_compose(dt, shape):
     # Small problems run both roles in one launch, the T=2100 ones (more than 512 64-key dK/dV
-    # workgroups) as two launches with the 128-key dK/dV kernel: either way the stage entry
+    # workgroups) as two launches with the separate dK/dV kernel: either way the stage entry
     # points must reproduce the one-call backward bitwise.
     B, T, Hq, Hkv, D = shape
     say("[inv] backward stages dt=%s shape=%s" % (dt, shape))

@@ -227,14 +227,14 @@ def test_backward_three_head_workgroups(case):
 
 
 @pytest.mark.parametrize("case", [(4, 2100, 12, 4, 64), (2, 2100, 16, 8, 64), (4, 2100, 4, 4, 32),
-                                  (72, 50, 24, 8, 64), (40, 100, 16, 16, 32)],
+                                  (72, 50, 24, 8, 64), (40, 100, 16, 16, 32), (2, 2100, 16, 8, 128)],
                          ids=lambda c: "B%d_T%d_H%d-%d_D%d" % c)
 def test_backward_separate_launches(case):
     # bf16 problems with more than 512 (64-key) dK/dV workgroups run the two backward roles as
-    # two launches: the 128-key dK/dV kernel, then the dQ-only kernel with six (three heads x
+    # two launches: the separate dK/dV kernel, then the dQ-only kernel with six (three heads x
     # two), eight (two heads x four) and four (one head x four) 32-row waves.  Ragged tails in
-    # every case; the last two are shorter than one 128-key tile (keys and query rows past the
-    # end inside the only tile).
+    # every case; two are shorter than one 128-key tile (keys and query rows past the end
+    # inside the only tile).  Head_dim 128 takes the four-wave 64-key dK/dV kernel.
     B, T, Hq, Hkv, D = case
     seed = 7900 + T + D + Hq
     say("[parity] backward as two launches, %s seed %d" % (case, seed))
