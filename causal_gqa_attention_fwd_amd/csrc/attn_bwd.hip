@@ -15,7 +15,9 @@
 //      registers; the workgroup walks every head of the group and every query tile on or
 //      below the diagonal, so dK and dV are group-summed in registers and written once.
 //      Q and dO tiles are staged row-major; the Q^T / dO^T operands of dK += dS^T Q and
-//      dV += P^T dO are read with gfx950's transposing LDS read.
+//      dV += P^T dO are read with gfx950's transposing LDS read.  Large bf16 problems take
+//      this role in a launch of its own (bwd_dkdv_kernel), with two 32-row query blocks per
+//      wave and, up to head_dim 64, 128-key workgroups.
 //   3. dQ role:   one workgroup per (query tile, K/V head, batch) over the G heads of the
 //      group, shaped like the forward: Q, dO, LSE and D stay in registers, K/V tiles stream
 //      through LDS shared by the group's heads, dQ is written once in the I/O dtype.
@@ -197,9 +199,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
     const int niter = g * nq;
 
     // Staging of Q_i / dO_i (16-byte chunks, row-major), LSE and D: HBM -> registers -> LDS,
-    // through NSET register sets (two for bf16 up to head_dim 64: each stage's loads then have
-    // two iterations to land; one for fp32 and for head_dim 128, whose registers are already
-    // spent on wider fragments and accumulators).
+    // through NSET register sets (two for bf16 up to head_dim 64 with one query block per wave:
+    // each stage's loads then have two iterations to land; one for fp32, for head_dim 128 and
+    // for two query blocks per wave, whose registers are already spent on wider fragments and
+    // accumulators).
     constexpr int NSET = (sizeof(T) == 2 && D < 128 && QB == 1) ? 2 : 1;
     struct Stg {
         Vec16<T> q[C::NCH], d[C::NCH];
