@@ -235,6 +235,53 @@ def time_decode(name, steps, warmup, torch, ea, W):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
+def time_fwd_rope(name, steps, warmup, torch, ea, W):
+    """The forward half of the step two ways on a workload's raw inputs: rope_apply_qk then
+    attn_fwd (the headline step's form), and attn_fwd_rope (K rotated in its own launch, which
+    also writes the (cos, sin) table; Q rotated inside the forward as it loads).  Microseconds
+    per call from HIP events around `steps` back-to-back calls on the launch stream."""
+    w = W.WORKLOADS[name]
+    log("[bench] fused-RoPE forward, workload %s" % name)
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = (inp[x].to(dev) for x in ("q_raw", "k_raw", "v"))
+    qr, kr, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T), device=dev, dtype=torch.float32)
+    L = ea.lib()
+    dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+    nws = L.attn_fwd_rope_workspace_size(w.T, w.D)
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    scale = 1.0 / (w.D ** 0.5)
+    p = lambda t: t.data_ptr()  # noqa: E731
+
+    def unfused():
+        if (L.rope_apply_qk(p(q), p(qr), w.Hq, p(k), p(kr), w.Hkv, w.B, w.T, w.D, dtc, w.base, 0, 0, stream)
+                or L.attn_fwd(p(qr), p(kr), p(v), p(o), p(lse), w.B, w.T, w.Hq, w.Hkv, w.D, scale, dtc, stream)):
+            raise RuntimeError("rope_apply_qk / attn_fwd failed")
+
+    def fused():
+        if L.attn_fwd_rope(p(q), p(k), p(v), p(o), p(lse), p(qr), p(kr), p(ws), nws, w.B, w.T, w.Hq, w.Hkv,
+                           w.D, scale, dtc, w.base, 0, stream):
+            raise RuntimeError("attn_fwd_rope failed")
+
+    res = {}
+    for label, fn in (("us_unfused", unfused), ("us_fused", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[label] = round(1000.0 * t0.elapsed_time(t1) / steps, 2)
+    return {"config": w.describe(), "calls": steps, **res,
+            "note": "two launches either way; the headline step keeps rope_apply_qk + attn_fwd"}
+
+
 def time_noncausal(name, steps, warmup, torch, ea, W):
     """attn_fwd_noncausal then attn_bwd_noncausal (its pre-pass and main launch) on the inputs
     of a workload (no RoPE): TFLOP/s at 14 * D * B * Hq * T^2 (every query/key pair), with the
@@ -419,11 +466,14 @@ def main() -> int:
     ap.add_argument("--noncausal", default="blog_t1024,long_t8192",
                     help="comma-separated workloads run through attn_fwd_noncausal + attn_bwd_noncausal, "
                          "reported under 'noncausal'; empty to skip")
+    ap.add_argument("--fwd-rope", default="blog_t1024,long_t8192",
+                    help="comma-separated workloads whose forward half is timed both as rope_apply_qk + "
+                         "attn_fwd and as attn_fwd_rope, reported under 'fwd_rope'; empty to skip")
     ap.add_argument("--proj", default="blog_t1024",
                     help="comma-separated workloads whose QKV / output projections (forward and backward) "
                          "are timed under 'projections'; empty to skip")
     ap.add_argument("--only", default="",
-                    help="profiling aid: comma-separated subset of extra,decode,projections,noncausal to run "
+                    help="profiling aid: comma-separated subset of extra,decode,projections,noncausal,fwd_rope to run "
                          "WITHOUT the headline step (prints those sections only, not the benchmark line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
@@ -470,6 +520,9 @@ def main() -> int:
             out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5),
                                                      torch, ea, W)
                                 for name in [x for x in args.noncausal.split(",") if x]}
+        if "fwd_rope" in want:
+            out["fwd_rope"] = {name: time_fwd_rope(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
+                               for name in [x for x in args.fwd_rope.split(",") if x]}
         print(json.dumps(out), flush=True)
         return 0
 
@@ -508,6 +561,8 @@ def main() -> int:
                           for name in [x for x in args.proj.split(",") if x]}
     out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5), torch, ea, W)
                         for name in [x for x in args.noncausal.split(",") if x]}
+    out["fwd_rope"] = {name: time_fwd_rope(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
+                       for name in [x for x in args.fwd_rope.split(",") if x]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on host cores")
         out["cpu_baseline"] = cpu_baseline(w, W)

@@ -28,7 +28,8 @@ import os
 
 import torch
 
-__all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
+__all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_rope",
+           "attn_fwd_rope_workspace_size", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
            "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "gemm",
            "qkv_proj", "qkv_proj_bwd", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = ci
     L.attn_fwd_noncausal.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_fwd_noncausal.restype = ci
+    L.attn_fwd_rope_workspace_size.argtypes = [ci, ci]
+    L.attn_fwd_rope_workspace_size.restype = sz
+    L.attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, cd, ci, vp]
+    L.attn_fwd_rope.restype = ci
     L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
     L.attn_bwd_workspace_size.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -192,6 +197,35 @@ def attn_fwd_noncausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale:
                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """GQA attention forward without the causal mask (every query sees every key)."""
     return _fwd("attn_fwd_noncausal", q, k, v, scale, out, lse)
+
+
+def attn_fwd_rope_workspace_size(T: int, D: int) -> int:
+    """Bytes of the workspace attn_fwd_rope needs (the RoPE (cos, sin) table)."""
+    return int(lib().attn_fwd_rope_workspace_size(T, D))
+
+
+def attn_fwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, base: float = 10000.0,
+                  pos0: int = 0, scale: float | None = None, workspace: torch.Tensor | None = None):
+    """RoPE on pre-rotation q and k fused with the causal GQA forward.
+
+    Returns (o, lse, q_r, k_r): the attention output and log-sum-exp as attn_fwd, and the
+    rotated q and k, which attn_bwd / attn_bwd_rope take as their q and k."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    l = torch.empty((B, Hq, T), device=q.device, dtype=torch.float32)
+    qr = torch.empty_like(q)
+    kr = torch.empty_like(k)
+    need = attn_fwd_rope_workspace_size(T, D)
+    ws = torch.empty(need, device=q.device, dtype=torch.uint8) if workspace is None else workspace
+    wp, wb = _ws_args(ws, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                                 qr.data_ptr(), kr.data_ptr(), wp, wb, B, T, Hq, Hkv, D, float(scale),
+                                 _dtype_code(q), float(base), int(pos0), _stream(q.device))
+    _raise(st, "attn_fwd_rope")
+    return o, l, qr, kr
 
 
 def _fwd(name, q, k, v, scale, out, lse):

@@ -124,6 +124,46 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
     return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, D, scale, dt, true, stream);
 }
 
+size_t attn_fwd_rope_workspace_size(int T, int D) {
+    if (T < 1 || D < 2 || (D % 2) != 0) return 0;
+    return ((size_t)T * (D / 2) * 2 * sizeof(float) + 255) & ~(size_t)255;
+}
+
+ea_status attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* q_r, void* k_r, void* workspace, size_t workspace_bytes, int B,
+                        int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, double base,
+                        int pos0, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !q_r || !k_r || !workspace) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    if (!std::isfinite(base) || !(base > 1.0) || pos0 < 0 || (long long)pos0 + T > (1LL << 31))
+        return EA_ERR_INVALID_ARG;
+    const size_t ws_need = attn_fwd_rope_workspace_size(T, D);
+    if (workspace_bytes < ws_need) return EA_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(lse),
+                          static_cast<const void*>(q_r), static_cast<const void*>(k_r),
+                          static_cast<const void*>(workspace)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const size_t es = elem_size(dt);
+    const Range ins[] = {range(q, (size_t)B * T * Hq * D * es), range(k, (size_t)B * T * Hkv * D * es),
+                         range(v, (size_t)B * T * Hkv * D * es)};
+    const Range outs[] = {range(o, (size_t)B * T * Hq * D * es), range(lse, (size_t)B * Hq * T * sizeof(float)),
+                          range(q_r, (size_t)B * T * Hq * D * es), range(k_r, (size_t)B * T * Hkv * D * es),
+                          range(workspace, ws_need)};
+    for (const Range& out : outs)
+        for (const Range& in : ins)
+            if (overlap(out, in)) return EA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return EA_ERR_ALIAS;
+    float* tab = static_cast<float*>(workspace);
+    const ea::IoType t = static_cast<ea::IoType>(dt);
+    const hipError_t e = ea::launch_rope_table(k, k_r, B, T, Hkv, D, t, base, pos0, tab, stream);
+    if (e != hipSuccess) return EA_ERR_HIP;
+    return from_hip(ea::launch_attn_fwd(q, k_r, v, o, lse, B, T, Hq, Hkv, D, scale, t, true, stream,
+                                        tab, q_r));
+}
+
 ea_status attn_fwd_noncausal(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
                              hipStream_t stream) {

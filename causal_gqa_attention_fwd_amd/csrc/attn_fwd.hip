@@ -55,6 +55,8 @@ struct FwdArgs {
     int ntq;  // query tiles
     int causal;  // 1: key s visible to query t iff s <= t; 0: every key visible
     float sl2;  // scale * log2(e)
+    const float* qtab;  // if set: q is pre-RoPE; (cos, sin) per (position, pair) rotate it
+    void* q_r;          // ... and the rotated rows are written here
 };
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest un-normalised P
@@ -284,6 +286,36 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     // Step s sits in register set s % NSET until it is committed at the start of step s - 1;
     // the set is then refilled with step s + NSET.
     fetch(sa, 0);
+    if (a.qtab != nullptr) {
+        // Queries given before RoPE: rotate each chunk's pairs (2p, 2p + 1) at its position with
+        // the (cos, sin) table and rope_apply's fp32 arithmetic, while the first K/V tile is in
+        // flight; the first key split writes the rotated rows out.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int t = q0 + qb * 32 + l32;
+            if (!active || t >= a.T) continue;
+            const long long roff = (((long long)b * a.T + t) * a.Hq + head) * D + half * (D / 2);
+#pragma unroll
+            for (int c = 0; c < (D / 2) / C::EPC; ++c) {
+                Vec16<T> v;
+#pragma unroll
+                for (int e = 0; e < C::EPC / KPL; ++e)
+                    reinterpret_cast<frag*>(&v.raw)[e] = qf[qb][c * (C::EPC / KPL) + e];
+                const float* tab = a.qtab + ((long long)t * (D / 2) + (half * (D / 2) + c * C::EPC) / 2) * 2;
+#pragma unroll
+                for (int p = 0; p < C::EPC / 2; ++p) {
+                    const float cs = tab[2 * p], sn = tab[2 * p + 1];
+                    const float x0 = to_f32(v.get(2 * p)), x1 = to_f32(v.get(2 * p + 1));
+                    v.set(2 * p, from_f32<T>(x0 * cs - x1 * sn));
+                    v.set(2 * p + 1, from_f32<T>(x0 * sn + x1 * cs));
+                }
+#pragma unroll
+                for (int e = 0; e < C::EPC / KPL; ++e)
+                    qf[qb][c * (C::EPC / KPL) + e] = reinterpret_cast<const frag*>(&v.raw)[e];
+                if (ks == 0) st16(static_cast<T*>(a.q_r) + roff + c * C::EPC, v);
+            }
+        }
+    }
     commit(sa, 0);
     if constexpr (NSET == 2) {
         if (nsteps > 1) fetch(sb, 1);
@@ -511,9 +543,11 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
-                           bool causal, hipStream_t stream) {
+                           bool causal, hipStream_t stream, const float* qtab, void* q_r) {
     FwdArgs a{};
     a.causal = causal ? 1 : 0;
+    a.qtab = qtab;
+    a.q_r = q_r;
     a.q = q;
     a.k = k;
     a.v = v;

@@ -18,6 +18,11 @@ struct RopeArgs {
 hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoType dt,
                        double base, int pos0, int inverse, hipStream_t stream);
 
+// RoPE of x into y (forward angles) that also writes the (cos, sin) table of every
+// (position, pair), fp32 [T, D/2, 2], into tab.
+hipError_t launch_rope_table(const void* x, void* y, int B, int T, int H, int D, IoType dt,
+                             double base, int pos0, float* tab, hipStream_t stream);
+
 // RoPE of two tensors sharing (B, T, D) in one launch: x0 [B,T,H0,D] -> y0, x1 [B,T,H1,D] -> y1.
 hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1,
                             int B, int T, int D, IoType dt, double base, int pos0, int inverse,
@@ -25,9 +30,12 @@ hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, vo
 
 // Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log); causal = false lets every query
 // see every key.
+// With qtab set, q holds the pre-RoPE queries: each row is rotated by the (cos, sin) table
+// (fp32 [T, D/2, 2]) as it loads, and the rotated rows are written to q_r.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
-                           bool causal, hipStream_t stream);
+                           bool causal, hipStream_t stream, const float* qtab = nullptr,
+                           void* q_r = nullptr);
 
 // Workspace of the backward: D_t = sum_d dO * O as fp32 [B, Hq, T], 256-byte aligned; with
 // rope, then the (cos, sin) table of the inverse RoPE, fp32 [T, D/2, 2], 256-byte aligned.

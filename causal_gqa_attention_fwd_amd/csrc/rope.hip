@@ -29,6 +29,7 @@ struct RopeJob {
     T* y[2];
     int H[2];
     long long n0, ntot;
+    float* tab;  // if set: (cos, sin) of every (position, pair), [T][D/2] float2 (forward angles)
 };
 
 // I: unsigned index type of the unit decomposition (32-bit whenever the units fit).
@@ -72,6 +73,13 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int 
         cs[p] = co;
         sn[p] = inverse ? -s : s;
     }
+    // The threads of batch 0 and head block 0 of the first tensor cover every (position, chunk)
+    // once: they write the table entries of their pairs.
+    if (job.tab != nullptr && which == 0 && hb == 0 && bt < seq) {
+#pragma unroll
+        for (int p = 0; p < PPC; ++p)
+            reinterpret_cast<float2*>(job.tab)[(long long)t * (D / 2) + c * PPC + p] = make_float2(cs[p], sn[p]);
+    }
 #pragma unroll
     for (int k = 0; k < kHeadsPerThread; ++k) {
         if (k < nh) {
@@ -90,7 +98,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int 
 
 template <typename T>
 hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1, int B,
-                         int seq, int D, double base, int pos0, int inverse, hipStream_t stream) {
+                         int seq, int D, double base, int pos0, int inverse, hipStream_t stream,
+                         float* tab = nullptr) {
     constexpr int EPC = 16 / sizeof(T);
     RopeFreq f;
     fill_rope_freq(&f, D, base);
@@ -101,6 +110,7 @@ hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void*
     job.x[1] = static_cast<const T*>(x1);
     job.y[1] = static_cast<T*>(y1);
     job.H[1] = H1;
+    job.tab = tab;
     auto units = [&](int H) {
         return H > 0 ? (long long)B * seq * ((H + kHeadsPerThread - 1) / kHeadsPerThread) * (D / EPC) : 0LL;
     };
@@ -124,6 +134,12 @@ hipError_t launch_rope(const void* x, void* y, int B, int T, int H, int D, IoTyp
                        double base, int pos0, int inverse, hipStream_t stream) {
     if (dt == kF32) return launch_rope_t<float>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, inverse, stream);
     return launch_rope_t<bf16>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, inverse, stream);
+}
+
+hipError_t launch_rope_table(const void* x, void* y, int B, int T, int H, int D, IoType dt,
+                             double base, int pos0, float* tab, hipStream_t stream) {
+    if (dt == kF32) return launch_rope_t<float>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, 0, stream, tab);
+    return launch_rope_t<bf16>(x, y, H, nullptr, nullptr, 0, B, T, D, base, pos0, 0, stream, tab);
 }
 
 hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, void* y1, int H1,

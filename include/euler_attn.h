@@ -92,6 +92,30 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * attn_fwd_rope -- rope_apply on q and k fused with attn_fwd: the rotary embedding that
+ * "Show HN: NanoEuler" (section 2) applies to queries and keys, then causal GQA attention on
+ * the rotated tensors.  Inputs are the pre-RoPE q [B,T,Hq,D] and k [B,T,Hkv,D], and v.  Two
+ * launches on stream: K is rotated once (into k_r), which also fills the (cos, sin) table of
+ * every (position, pair) in the workspace; the forward then rotates each query row as it
+ * loads it (queries stay in registers for the whole key loop, so each is rotated once) and
+ * writes it to q_r.  Outputs: o, lse as attn_fwd; q_r, k_r the rotated q and k in dt, the
+ * inputs attn_bwd / attn_bwd_rope need.  Angles and arithmetic are rope_apply's (base, pos0,
+ * adjacent pairs; float64 angle reduction, float32 rotation); k_r equals rope_apply's output
+ * bitwise.
+ * workspace: at least attn_fwd_rope_workspace_size(T, D) bytes, 16-byte aligned, contents on
+ * entry don't care (attn_fwd_rope_workspace_size returns 0 for T < 1 or D odd or < 2).
+ * Errors: as attn_fwd, plus NULL q_r, k_r or workspace (EA_ERR_NULL); base <= 1 or not finite,
+ * pos0 < 0 (EA_ERR_INVALID_ARG); workspace too small (EA_ERR_WORKSPACE); any of o, lse, q_r,
+ * k_r, workspace overlapping q, k, v or each other (EA_ERR_ALIAS: no output may alias an
+ * input here, in-place rotation included).
+ */
+size_t attn_fwd_rope_workspace_size(int T, int D);
+ea_status attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* q_r, void* k_r, void* workspace, size_t workspace_bytes, int B,
+                        int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, double base,
+                        int pos0, hipStream_t stream);
+
+/*
  * attn_fwd_noncausal -- attn_fwd without the causal mask: every query row sees every key row,
  * S_ts = scale * <q_t, k_s> for all s in [0, T);  O_t = sum_s softmax_s(S_t.) v_s;
  * LSE_t = log sum_s exp(S_ts).  This is the form of the tiled FlashAttention forward that the

@@ -38,7 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rope_apply", "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_rope",
+    for n in ("rope_apply", "attn_fwd", "attn_fwd_rope", "attn_fwd_rope_workspace_size", "attn_bwd",
+              "attn_bwd_workspace_size", "attn_bwd_rope",
               "attn_fwd_noncausal", "attn_bwd_noncausal", "attn_decode",
               "attn_bwd_rope_workspace_size", "euler_attn_status_string", "euler_attn_version"):
         assert n in names
@@ -221,6 +222,32 @@ def test_bwd_rope_validation(L):
     assert mn(dq=None) == NULL
     assert mn(wb=L.attn_bwd_workspace_size(2, 16, 4, 2, 64, BF16)) == WS
     assert mn(dq=fake(8)) == ALIAS
+
+
+def test_fwd_rope_workspace_and_validation(L):
+    # The (cos, sin) table of every (position, pair): fp32 [T, D/2, 2], rounded to 256 bytes.
+    for (T, D) in ((1024, 64), (3, 32), (4096, 128)):
+        assert L.attn_fwd_rope_workspace_size(T, D) == (T * D * 4 + 255) // 256 * 256
+    assert L.attn_fwd_rope_workspace_size(0, 64) == 0
+    assert L.attn_fwd_rope_workspace_size(16, 7) == 0
+    ws = L.attn_fwd_rope_workspace_size(16, 64)
+
+    def fr(q=fake(0), k=fake(1), v=fake(2), o=fake(3), lse=fake(4), qr=fake(5), kr=fake(6), w=fake(7),
+           wb=ws, T=16, D=64, Hq=4, Hkv=2, scale=0.125, dt=BF16, base=1e4, pos0=0):
+        return L.attn_fwd_rope(q, k, v, o, lse, qr, kr, w, wb, 2, T, Hq, Hkv, D, scale, dt, base, pos0, None)
+    for name in ("q", "k", "v", "o", "lse", "qr", "kr", "w"):
+        assert fr(**{name: None}) == NULL, name
+    for kw in (dict(Hq=3), dict(scale=0.0), dict(base=1.0), dict(base=float("nan")), dict(pos0=-1),
+               dict(pos0=(1 << 31) - 8)):
+        assert fr(**kw) == INVALID, kw
+    assert fr(D=96) == UNSUP
+    assert fr(dt=3) == UNSUP
+    assert fr(wb=ws - 1) == WS
+    assert fr(qr=fake(5) + 8) == ALIGN
+    assert fr(qr=fake(0)) == ALIAS        # in-place rotation of q is not allowed here
+    assert fr(kr=fake(1)) == ALIAS
+    assert fr(w=fake(3) + 256) == ALIAS   # workspace inside o
+    assert fr(kr=fake(5)) == ALIAS        # q_r and k_r overlap
 
 
 def test_decode_workspace_and_validation(L):
