@@ -91,7 +91,7 @@ ea_status rope_apply(const void* x, void* y, int B, int T, int H, int D, ea_dtyp
     if (x == nullptr || y == nullptr) return EA_ERR_NULL;
     if (B < 1 || T < 1 || H < 1 || D < 2 || (D % 2) != 0 || pos0 < 0) return EA_ERR_INVALID_ARG;
     if (!std::isfinite(base) || !(base > 1.0) || (inverse != 0 && inverse != 1)) return EA_ERR_INVALID_ARG;
-    if (!dtype_ok(dt) || D > 256 || (D % 8) != 0) return EA_ERR_UNSUPPORTED;
+    if (!dtype_ok(dt) || D > 256) return EA_ERR_UNSUPPORTED;
     if ((long long)pos0 + T > (1LL << 31)) return EA_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(y)) return EA_ERR_ALIGN;
     const size_t bytes = (size_t)B * T * H * D * elem_size(dt);
@@ -106,7 +106,7 @@ ea_status rope_apply_qk(const void* q, void* q_out, int Hq, const void* k, void*
     if (!q || !q_out || !k || !k_out) return EA_ERR_NULL;
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 2 || (D % 2) != 0 || pos0 < 0) return EA_ERR_INVALID_ARG;
     if (!std::isfinite(base) || !(base > 1.0) || (inverse != 0 && inverse != 1)) return EA_ERR_INVALID_ARG;
-    if (!dtype_ok(dt) || D > 256 || (D % 8) != 0) return EA_ERR_UNSUPPORTED;
+    if (!dtype_ok(dt) || D > 256) return EA_ERR_UNSUPPORTED;
     if ((long long)pos0 + T > (1LL << 31)) return EA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(q_out) || !aligned16(k) || !aligned16(k_out)) return EA_ERR_ALIGN;
     const size_t es = elem_size(dt);

@@ -427,9 +427,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const float x0 = x[e + 2 * u], x1 = x[e + 2 * u + 1];
-                    const float cs = w[2 * u], sn = w[2 * u + 1];
-                    x[e + 2 * u] = x0 * cs + x1 * sn;
-                    x[e + 2 * u + 1] = x1 * cs - x0 * sn;
+                    rope_rotate(x0, x1, w[2 * u], -w[2 * u + 1], &x[e + 2 * u], &x[e + 2 * u + 1]);
                 }
             }
         }
@@ -667,10 +665,13 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
                 f32x16& x = dqacc[db];
                 const int r = 4 * a4;
                 const float x0 = x[r], x1 = x[r + 1], x2 = x[r + 2], x3 = x[r + 3];
-                x[r] = x0 * w.x + x1 * w.y;
-                x[r + 1] = x1 * w.x - x0 * w.y;
-                x[r + 2] = x2 * w.z + x3 * w.w;
-                x[r + 3] = x3 * w.z - x2 * w.w;
+                float y0, y1, y2, y3;
+                rope_rotate(x0, x1, w.x, -w.y, &y0, &y1);
+                rope_rotate(x2, x3, w.z, -w.w, &y2, &y3);
+                x[r] = y0;
+                x[r + 1] = y1;
+                x[r + 2] = y2;
+                x[r + 3] = y3;
             }
     }
     T* __restrict__ dqp = static_cast<T*>(a.dq);

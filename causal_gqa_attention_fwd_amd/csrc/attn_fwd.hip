@@ -304,10 +304,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
                 const float* tab = a.qtab + ((long long)t * (D / 2) + (half * (D / 2) + c * C::EPC) / 2) * 2;
 #pragma unroll
                 for (int p = 0; p < C::EPC / 2; ++p) {
-                    const float cs = tab[2 * p], sn = tab[2 * p + 1];
-                    const float x0 = to_f32(v.get(2 * p)), x1 = to_f32(v.get(2 * p + 1));
-                    v.set(2 * p, from_f32<T>(x0 * cs - x1 * sn));
-                    v.set(2 * p + 1, from_f32<T>(x0 * sn + x1 * cs));
+                    float y0, y1;
+                    rope_rotate(to_f32(v.get(2 * p)), to_f32(v.get(2 * p + 1)), tab[2 * p], tab[2 * p + 1], &y0, &y1);
+                    v.set(2 * p, from_f32<T>(y0));
+                    v.set(2 * p + 1, from_f32<T>(y1));
                 }
 #pragma unroll
                 for (int e = 0; e < C::EPC / KPL; ++e)

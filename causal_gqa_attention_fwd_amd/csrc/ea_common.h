@@ -224,4 +224,14 @@ __device__ inline void rope_cos_sin(double pos, double theta, float* c, float* s
     sincosf((float)r, s, c);
 }
 
+// Rotation of one RoPE pair (x0, x1) by the angle with cosine c and sine s:
+//   y0 = x0 c - x1 s,   y1 = x0 s + x1 c.
+// The evaluation order is fixed (one product, then one fused multiply-add per output), so
+// every kernel that rotates a pair rounds it the same way whatever the compiler would have
+// contracted; the inverse rotation passes -s.
+__device__ inline void rope_rotate(float x0, float x1, float c, float s, float* y0, float* y1) {
+    *y0 = __builtin_fmaf(x0, c, -(x1 * s));
+    *y1 = __builtin_fmaf(x0, s, x1 * c);
+}
+
 }  // namespace ea

@@ -402,8 +402,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
                         float co, sn;
                         rope_cos_sin((double)g.rope_pos0 + (double)t, g.f.theta[(d0 + e) >> 1], &co, &sn);
                         const float x0 = x[e], x1 = x[e + 1];
-                        x[e] = x0 * co - x1 * sn;
-                        x[e + 1] = x0 * sn + x1 * co;
+                        rope_rotate(x0, x1, co, sn, &x[e], &x[e + 1]);
                     }
                 }
                 T* cp = const_cast<T*>(sc_.at(m, n));

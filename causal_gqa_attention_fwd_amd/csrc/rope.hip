@@ -10,7 +10,8 @@
 // a row (8 bf16 or 4 fp32 elements) for HPT heads of the same position: the angles of its
 // pairs are formed once, in float64 (product and reduction modulo 2*pi), and reused for
 // every head.  sin/cos of the reduced angle, |r| <= pi, are float32.  Consecutive lanes
-// take consecutive chunks of a row, so each wave reads whole 128-byte rows.
+// take consecutive chunks of a row, so each wave reads whole 128-byte rows.  Head dims that
+// are not a whole number of chunks (any other even D up to 256) take one thread per pair.
 #include <cmath>
 
 #include "ea_common.h"
@@ -86,14 +87,58 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int 
             Vec16<T> w;
 #pragma unroll
             for (int p = 0; p < PPC; ++p) {
-                const float x0 = to_f32(v[k].get(2 * p));
-                const float x1 = to_f32(v[k].get(2 * p + 1));
-                w.set(2 * p, from_f32<T>(x0 * cs[p] - x1 * sn[p]));
-                w.set(2 * p + 1, from_f32<T>(x0 * sn[p] + x1 * cs[p]));
+                float y0, y1;
+                rope_rotate(to_f32(v[k].get(2 * p)), to_f32(v[k].get(2 * p + 1)), cs[p], sn[p], &y0, &y1);
+                w.set(2 * p, from_f32<T>(y0));
+                w.set(2 * p + 1, from_f32<T>(y1));
             }
             st16(y + off0 + (long long)k * D, w);
         }
     }
+}
+
+// Head dims that are not a whole number of 16-byte chunks (D = 2, 6, 10, ... for bf16; D = 2,
+// 6, ... for fp32): one thread per pair (2i, 2i+1) of one position, for kHeadsPerThread heads,
+// with the same angle and rotation arithmetic as rope_kernel.  A pair is 4 (bf16) or 8 (fp32)
+// bytes and always aligned to its size, since D is even.
+template <typename T, typename I>
+__global__ __launch_bounds__(256) void rope_pair_kernel(RopeJob<T> job, int seq, int D, int pos0,
+                                                        int inverse, RopeFreq f) {
+    I u = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
+    if (u >= (I)job.ntot) return;
+    const int which = u < (I)job.n0 ? 0 : 1;
+    if (which) u -= (I)job.n0;
+    const T* x = job.x[which];
+    T* y = job.y[which];
+    const int H = job.H[which];
+    const I ppr = (I)(D / 2);  // pairs per row
+    const I nhb = (I)((H + kHeadsPerThread - 1) / kHeadsPerThread);
+    const int i = (int)(u % ppr);
+    const I rest = u / ppr;
+    const int hb = (int)(rest % nhb);
+    const long long bt = (long long)(rest / nhb);
+    const int t = (int)(bt % seq);
+    const int h0 = hb * kHeadsPerThread;
+    const int nh = min(H - h0, kHeadsPerThread);
+    const long long off0 = (bt * H + h0) * (long long)D + 2LL * i;
+    T v[kHeadsPerThread][2];
+#pragma unroll
+    for (int k = 0; k < kHeadsPerThread; ++k)
+        if (k < nh) {
+            v[k][0] = x[off0 + (long long)k * D];
+            v[k][1] = x[off0 + (long long)k * D + 1];
+        }
+    float c, s;
+    rope_cos_sin((double)pos0 + (double)t, f.theta[i], &c, &s);
+    if (inverse) s = -s;
+#pragma unroll
+    for (int k = 0; k < kHeadsPerThread; ++k)
+        if (k < nh) {
+            float y0, y1;
+            rope_rotate(to_f32(v[k][0]), to_f32(v[k][1]), c, s, &y0, &y1);
+            y[off0 + (long long)k * D] = from_f32<T>(y0);
+            y[off0 + (long long)k * D + 1] = from_f32<T>(y1);
+        }
 }
 
 template <typename T>
@@ -111,19 +156,30 @@ hipError_t launch_rope_t(const void* x0, void* y0, int H0, const void* x1, void*
     job.y[1] = static_cast<T*>(y1);
     job.H[1] = H1;
     job.tab = tab;
+    // Whole 16-byte chunks per row: one thread per chunk; otherwise one thread per pair.
+    const bool chunks = D % EPC == 0;
+    if (!chunks && tab != nullptr) return hipErrorInvalidValue;  // the table path needs chunks
+    const int per_row = chunks ? D / EPC : D / 2;
     auto units = [&](int H) {
-        return H > 0 ? (long long)B * seq * ((H + kHeadsPerThread - 1) / kHeadsPerThread) * (D / EPC) : 0LL;
+        return H > 0 ? (long long)B * seq * ((H + kHeadsPerThread - 1) / kHeadsPerThread) * per_row : 0LL;
     };
     job.n0 = units(H0);
     job.ntot = job.n0 + units(H1);
     const int threads = 256;
     const long long blocks = (job.ntot + threads - 1) / threads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (blocks * threads <= 0xffffffffLL)
+    const bool narrow = blocks * threads <= 0xffffffffLL;
+    if (chunks && narrow)
         hipLaunchKernelGGL((rope_kernel<T, uint32_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
                            job, seq, D, pos0, inverse, f);
-    else
+    else if (chunks)
         hipLaunchKernelGGL((rope_kernel<T, uint64_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           job, seq, D, pos0, inverse, f);
+    else if (narrow)
+        hipLaunchKernelGGL((rope_pair_kernel<T, uint32_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           job, seq, D, pos0, inverse, f);
+    else
+        hipLaunchKernelGGL((rope_pair_kernel<T, uint64_t>), dim3((unsigned)blocks), dim3(threads), 0, stream,
                            job, seq, D, pos0, inverse, f);
     return hipGetLastError();
 }

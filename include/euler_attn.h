@@ -61,6 +61,9 @@ typedef enum {
  * backward of the forward rotation (the rotation is orthogonal): apply it to dQ and dK to
  * obtain gradients with respect to the pre-RoPE tensors.  The angle is formed and reduced
  * modulo 2*pi in float64; sin/cos of the reduced angle and the rotation are float32.
+ * Every even D from 2 to 256 is accepted: head dims that are a whole number of 16-byte
+ * chunks (D a multiple of 8 for bf16, of 4 for fp32) are moved in 16-byte pieces, any other
+ * even D pair by pair, with the same arithmetic.
  * y == x (exactly) is allowed (in place); any other overlap is EA_ERR_ALIAS.
  * Errors: NULL x or y; B, T, H < 1, D odd or < 2, pos0 < 0, base <= 1 or not finite,
  * inverse not 0/1 (EA_ERR_INVALID_ARG); D > 256 or unknown dt (EA_ERR_UNSUPPORTED).

@@ -68,7 +68,6 @@ def test_rope_validation(L):
                dict(base=1.0), dict(base=float("nan")), dict(base=float("inf")), dict(inv=2)):
         assert rope(L, **kw) == INVALID, kw
     assert rope(L, D=258) == UNSUP
-    assert rope(L, D=6) == UNSUP          # not a multiple of 8
     assert rope(L, dt=5) == UNSUP
     assert rope(L, x=fake(0) + 4) == ALIGN
     assert rope(L, y=fake(0) + 16) == ALIAS  # partial overlap
@@ -81,7 +80,7 @@ def test_rope_qk_validation(L):
     assert r(k=None) == NULL
     assert r(Hkv=0) == INVALID
     assert r(inv=3) == INVALID
-    assert r(D=12) == UNSUP
+    assert r(D=258) == UNSUP
     assert r(ko=fake(3) + 8) == ALIGN
     assert r(ko=fake(2) + 64) == ALIAS          # k_out partially over k
     assert r(qo=fake(2)) == ALIAS               # q_out over k
@@ -345,3 +344,4 @@ def test_qkv_proj_bwd_validation(L):
     assert call(dx=fake(5) + 2) == ALIGN
     assert call(dx=fake(1)) == ALIAS                    # dx over w
     assert call(dw=fake(5) + 64) == ALIAS               # dw over dx
+

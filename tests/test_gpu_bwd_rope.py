@@ -60,11 +60,13 @@ def test_bwd_rope_workload(name):
         assert max(e2e.values()) <= TOL["f32"]["grad"]
 
 
-@pytest.mark.parametrize("name,b,kv", [("long_t8192", 1, 2), ("gqa_t4096_d128", 5, 3)])
-def test_bwd_rope_full_size_sampled(name, b, kv):
+# Slices: an interior one, the first (0, 0) and the last (B-1, Hkv-1) of the launch grid.
+@pytest.mark.parametrize("name,slices", [("long_t8192", [(1, 2), (0, 0), (1, 3)]),
+                                         ("gqa_t4096_d128", [(5, 3), (0, 0), (7, 7)])])
+def test_bwd_rope_full_size_sampled(name, slices):
     w = W.WORKLOADS[name]
     g = w.g
-    say("[parity] attn_bwd_rope workload %s (full size on GPU, oracle on slice b=%d kv=%d)" % (name, b, kv))
+    say("[parity] attn_bwd_rope workload %s (full size on GPU, oracle on slices %s)" % (name, slices))
     inp = W.make_inputs(w)
     q, k, v, qr, kr, o, lse = gpu_forward_pipeline(inp, w.base)
     do = inp["dout"].cuda()
@@ -72,11 +74,13 @@ def test_bwd_rope_full_size_sampled(name, b, kv):
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t).all())
-    hs = slice(kv * g, (kv + 1) * g)
-    ref = oracle_fused(qr[b:b + 1, :, hs], kr[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1],
-                       do[b:b + 1, :, hs], w.base)
-    check_grads(w.dtype, {"dq": dq[b:b + 1, :, hs], "dk": dk[b:b + 1, :, kv:kv + 1],
-                          "dv": dv[b:b + 1, :, kv:kv + 1]}, ref, "bwd_rope slice")
+    for b, kv in slices:
+        say(" slice b=%d kv=%d" % (b, kv))
+        hs = slice(kv * g, (kv + 1) * g)
+        ref = oracle_fused(qr[b:b + 1, :, hs], kr[b:b + 1, :, kv:kv + 1], v[b:b + 1, :, kv:kv + 1],
+                           do[b:b + 1, :, hs], w.base)
+        check_grads(w.dtype, {"dq": dq[b:b + 1, :, hs], "dk": dk[b:b + 1, :, kv:kv + 1],
+                              "dv": dv[b:b + 1, :, kv:kv + 1]}, ref, "bwd_rope slice b=%d kv=%d" % (b, kv))
 
 
 EDGE = [(1, 1, 1, 1, 32, "f32", 0, 1e4), (2, 17, 4, 1, 64, "bf16", 3, 1e4),

@@ -67,8 +67,9 @@ def test_workload_full(name):
         assert max(e2e.values()) <= 1e-3
 
 
-@pytest.mark.parametrize("name,slices", [("long_t8192", [(1, 2), (0, 0)]),
-                                         ("gqa_t4096_d128", [(5, 3)])])
+# Slices: an interior one, the first (0, 0) and the last (B-1, Hkv-1) of the launch grid.
+@pytest.mark.parametrize("name,slices", [("long_t8192", [(1, 2), (0, 0), (1, 3)]),
+                                         ("gqa_t4096_d128", [(5, 3), (0, 0), (7, 7)])])
 def test_workload_full_size_sampled(name, slices):
     w = W.WORKLOADS[name]
     g = w.g
@@ -137,7 +138,12 @@ def test_edge_sweep(case):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("D,H,T,base,pos0", [(32, 3, 33, 1e4, 0), (64, 12, 129, 1e4, 7),
                                              (128, 8, 70, 5e5, 4000), (8, 1, 5, 1e4, 0),
-                                             (256, 2, 9, 1e4, 1)])
+                                             (256, 2, 9, 1e4, 1),
+                                             # head dims that are not whole 16-byte chunks
+                                             # (pair by pair), and 12 (chunks for fp32 only)
+                                             (2, 3, 9, 1e4, 0), (6, 5, 17, 1e4, 3),
+                                             (10, 2, 40, 5e5, 100), (12, 4, 33, 1e4, 0),
+                                             (254, 1, 6, 1e4, 2)])
 def test_rope_variants(dt, D, H, T, base, pos0):
     say("[parity] rope dt=%s D=%d H=%d T=%d base=%g pos0=%d" % (dt, D, H, T, base, pos0))
     x = W.make_random((2, T, H, D), 99 + D + T, dt).cuda()
@@ -153,12 +159,14 @@ def test_rope_variants(dt, D, H, T, base, pos0):
     assert torch.equal(z, y)
 
 
+@pytest.mark.parametrize("D", [64, 6])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_rope_qk_one_launch(dt):
-    # The two-tensor launch equals two single-tensor launches bitwise, and the oracle.
-    say("[parity] rope_apply_qk dt=%s" % dt)
-    q = W.make_random((2, 77, 12, 64), 501, dt).cuda()
-    k = W.make_random((2, 77, 4, 64), 502, dt).cuda()
+def test_rope_qk_one_launch(dt, D):
+    # The two-tensor launch equals two single-tensor launches bitwise, and the oracle; D = 6
+    # takes the pair-by-pair kernel.
+    say("[parity] rope_apply_qk dt=%s D=%d" % (dt, D))
+    q = W.make_random((2, 77, 12, D), 501, dt).cuda()
+    k = W.make_random((2, 77, 4, D), 502, dt).cuda()
     for inverse in (False, True):
         qo, ko = ea.rope_apply_qk(q, k, 10000.0, pos0=3, inverse=inverse)
         q1 = ea.rope_apply(q, 10000.0, pos0=3, inverse=inverse)
