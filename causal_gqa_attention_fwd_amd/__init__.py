@@ -11,6 +11,7 @@ built, or the tensors are not on a ROCm device, the calls raise.
     attn_bwd(q, k, v, o, lse, dout, scale=None, ...)         -> (dq, dk, dv)
     attn_bwd_rope(q, k, v, o, lse, dout, base=1e4, pos0=0, ...)
                          -> (dq, dk, dv) with dq, dk for the tensors before RoPE
+    attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv)        -> attn_bwd, no allocation
     attn_decode(q, k_cache, v_cache, scale=None, ...)         -> (o, lse) for the last Tq rows
     attn_fwd_noncausal / attn_bwd_noncausal                   -> as attn_fwd / attn_bwd, no mask
     gemm(a, b, trans_a=False, trans_b=False, out=None)        -> op(a) @ op(b)
@@ -32,12 +33,16 @@ __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "att
            "attn_fwd_rope_workspace_size", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
            "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "gemm",
-           "qkv_proj", "qkv_proj_bwd", "lib", "LIB_PATH", "EA_F32", "EA_BF16", "STATUS"]
+           "qkv_proj", "qkv_proj_bwd", "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH", "EA_F32",
+           "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
 EA_F32, EA_BF16 = 0, 1
 STATUS = {0: "EA_OK", 1: "EA_ERR_NULL", 2: "EA_ERR_INVALID_ARG", 3: "EA_ERR_UNSUPPORTED",
-          4: "EA_ERR_ALIGN", 5: "EA_ERR_ALIAS", 6: "EA_ERR_WORKSPACE", 7: "EA_ERR_HIP"}
+          4: "EA_ERR_ALIGN", 5: "EA_ERR_ALIAS", 6: "EA_ERR_WORKSPACE", 7: "EA_ERR_HIP",
+          8: "EA_ERR_SCRATCH"}
+# Bytes of the static device scratch behind attn_bwd_noalloc (EA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -70,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.restype = ci
     L.attn_bwd_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_bwd_noncausal.restype = ci
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_bwd_noalloc.restype = ci
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, vp]
     L.attn_bwd_preprocess.restype = ci
     L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -263,6 +270,32 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
     """Causal GQA attention backward; returns (dq, dk, dv), dk/dv summed over each group."""
     return _bwd(q, k, v, o, lse, dout, scale, workspace, dq, dk, dv, None)
+
+
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, dout: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+                     dv: torch.Tensor, scale: float | None = None):
+    """attn_bwd without a workspace: D_t goes to the library's static per-device scratch, so
+    nothing is allocated (the caller passes the outputs).  Calls that overlap in time on one
+    device race on that scratch.  Returns (dq, dk, dv)."""
+    B, T, Hq, Hkv, D = _shapes(q, k, v)
+    _check("o", o, 4, q.device, q.dtype)
+    _check("dout", dout, 4, q.device, q.dtype)
+    _check("lse", lse, 3, q.device, torch.float32)
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("o/dout must match q and lse must be [B, Hq, T]")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check(name, t, 4, q.device, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError("%s has the wrong shape" % name)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, T, Hq,
+                                    Hkv, D, float(scale), _dtype_code(q), _stream(q.device))
+    _raise(st, "attn_bwd_noalloc")
+    return dq, dk, dv
 
 
 def attn_bwd_noncausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

@@ -3,11 +3,18 @@
 // Every entry point validates all of its arguments before anything is enqueued (no HIP
 // call happens on an invalid call), then hands off to the internal launchers.  Nothing is
 // allocated, freed or synchronised here.  Declarations and the contract: euler_attn.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "ea_kernels.h"
 #include "euler_attn.h"
+
+// Scratch of attn_bwd_noalloc: D_t of one backward call, in a fixed array that each device
+// holds for the life of the process.  In host code this name is only a handle for the
+// symbol lookup below: kernels receive the per-device address that the lookup returns.
+static __device__ __align__(256) unsigned char scratch[EA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -80,6 +87,9 @@ const char* euler_attn_status_string(ea_status s) {
         case EA_ERR_ALIAS: return "EA_ERR_ALIAS: an output overlaps an input or another output";
         case EA_ERR_WORKSPACE: return "EA_ERR_WORKSPACE: workspace smaller than attn_bwd_workspace_size()";
         case EA_ERR_HIP: return "EA_ERR_HIP: the HIP runtime reported an error at launch";
+        case EA_ERR_SCRATCH:
+            return "EA_ERR_SCRATCH: the problem needs more scratch than attn_bwd_noalloc's static "
+                   "buffer (EA_NOALLOC_SCRATCH_BYTES) holds";
     }
     return "unknown euler_attn status";
 }
@@ -407,6 +417,62 @@ ea_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* 
     if ((st = check_alias(ins, outs)) != EA_OK) return st;
     return from_hip(ea::launch_bwd_dq(q, k, v, lse, dout, dq, const_cast<void*>(workspace), B, T,
                                       Hq, Hkv, D, scale, static_cast<ea::IoType>(dt), stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+ea_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EA_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return EA_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                           hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return EA_ERR_NULL;
+    ea_status st = check_attn_sizes(B, T, Hq, Hkv, D, scale, dt);
+    if (st != EA_OK) return st;
+    for (const void* p : {q, k, v, o, static_cast<const void*>(lse), dout,
+                          static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+        if (!aligned16(p)) return EA_ERR_ALIGN;
+    const BwdSizes z = bwd_sizes(B, T, Hq, Hkv, D, dt);
+    if (z.ws > (size_t)EA_NOALLOC_SCRATCH_BYTES) return EA_ERR_SCRATCH;
+    const Range ins[] = {range(q, z.qb), range(k, z.kb), range(v, z.kb), range(o, z.qb),
+                         range(lse, z.lseb), range(dout, z.qb)};
+    const Range outs[] = {range(dq, z.qb), range(dk, z.kb), range(dv, z.kb)};
+    if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != EA_OK) return st;
+    // The same two stages as attn_bwd; the pre-pass writes every D_t entry the main stage
+    // reads, so nothing left in the scratch by an earlier call is ever read.
+    return from_hip(ea::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, T, Hq, Hkv, D,
+                                        scale, static_cast<ea::IoType>(dt), nullptr, true, stream));
 }
 
 }  // extern "C"

@@ -44,7 +44,8 @@ typedef enum {
     EA_ERR_ALIGN = 4,         /* a tensor pointer is not 16-byte aligned                  */
     EA_ERR_ALIAS = 5,         /* an output overlaps an input or another output            */
     EA_ERR_WORKSPACE = 6,     /* workspace smaller than attn_bwd_workspace_size()         */
-    EA_ERR_HIP = 7            /* the HIP runtime reported an error at launch              */
+    EA_ERR_HIP = 7,           /* the HIP runtime reported an error at launch              */
+    EA_ERR_SCRATCH = 8        /* attn_bwd_noalloc: the problem exceeds its static scratch */
 } ea_status;
 
 typedef enum {
@@ -185,6 +186,25 @@ ea_status attn_bwd_noncausal(const void* q, const void* k, const void* v, const 
                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, int B, int T, int Hq,
                              int Hkv, int D, float scale, ea_dtype dt, hipStream_t stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving or training loops, harnesses that forbid
+ * hipMalloc.  Same arguments as attn_bwd minus the workspace, same kernels, same outputs
+ * bitwise.  D_t goes to a static device array of EA_NOALLOC_SCRATCH_BYTES (16 MiB) that the
+ * library holds on every device it runs on until the process ends; the call allocates and
+ * frees nothing.  Limit: attn_bwd_workspace_size(B, T, Hq, Hkv, D, dt) must not exceed
+ * EA_NOALLOC_SCRATCH_BYTES (B * Hq * T <= 4 Mi rows), else EA_ERR_SCRATCH before anything
+ * is enqueued.  Every call on one device shares that device's array: calls that overlap in
+ * time on one device (two streams, two host threads) race and must be serialised by the
+ * caller.  The stream must belong to the current device.  Errors: as attn_bwd (no
+ * workspace checks), EA_ERR_SCRATCH, and EA_ERR_HIP if the array's address cannot be found.
+ */
+#define EA_NOALLOC_SCRATCH_BYTES (16u << 20)
+ea_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int T, int Hq, int Hkv, int D, float scale, ea_dtype dt,
+                           hipStream_t stream);
 
 /*
  * The stages of attn_bwd, for callers that schedule them separately: attn_bwd is exactly

@@ -13,7 +13,7 @@ import causal_gqa_attention_fwd_amd as ea
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "euler_attn.h")
 
-OK, NULL, INVALID, UNSUP, ALIGN, ALIAS, WS, HIP = range(8)
+OK, NULL, INVALID, UNSUP, ALIGN, ALIAS, WS, HIP, SCRATCH = range(9)
 F32, BF16 = 0, 1
 A = 1 << 32  # fake, 256-byte aligned "device" addresses, far apart
 
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    for code in range(8):
+    for code in range(9):
         s = L.euler_attn_status_string(code).decode()
         assert s.startswith(ea.STATUS[code])
     assert L.euler_attn_version() >= 100
@@ -345,3 +345,20 @@ def test_qkv_proj_bwd_validation(L):
     assert call(dx=fake(1)) == ALIAS                    # dx over w
     assert call(dw=fake(5) + 64) == ALIAS               # dw over dx
 
+
+def test_noalloc_validation(L):
+    # attn_bwd_noalloc validates like attn_bwd (no workspace) and rejects a problem whose D_t
+    # exceeds the static scratch before any HIP call.
+    def nb(q=fake(0), dq=fake(6), dk=fake(7), B=2, T=16, Hq=4, Hkv=2, D=64, scale=0.125, dt=BF16):
+        return L.attn_bwd_noalloc(q, fake(1), fake(2), fake(3), fake(4), fake(5), dq, dk, fake(8),
+                                  B, T, Hq, Hkv, D, scale, dt, None)
+    assert nb(q=None) == NULL
+    assert nb(Hq=3) == INVALID
+    assert nb(D=48) == UNSUP
+    assert nb(dk=fake(7) + 4) == ALIGN
+    assert nb(dq=fake(0)) == ALIAS
+    # B * Hq * T = 4 Mi rows fits exactly (16 MiB of D_t); one more position does not.  With
+    # these sizes the fake tensors overlap, so the scratch check must come first.
+    assert nb(B=64, Hq=64, Hkv=64, T=1025, D=32) == SCRATCH
+    assert ea.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert L.attn_bwd_workspace_size(64, 1024, 64, 64, 32, BF16) == ea.NOALLOC_SCRATCH_BYTES
