@@ -174,8 +174,10 @@ def roofline_for(w, kern_us, name):
     try:
         with open(TRAFFIC_FILE) as f:
             tc = json.load(f)
-        ent = tc.get("kernels", {}).get(name)
-        if (ent and ent.get("workload") == w.name and name in KERNEL_SOURCES
+        # Entries are keyed "<entry point>@<workload>"; a figure counts only while the
+        # kernel sources still hash to the value recorded with it.
+        ent = tc.get("kernels", {}).get("%s@%s" % (name, w.name))
+        if (ent and name in KERNEL_SOURCES
                 and ent.get("source_sha") == sources_sha(KERNEL_SOURCES[name])):
             traffic = ent.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -406,35 +408,95 @@ def time_projections(name, steps, warmup, torch, ea, W):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, W):
-    """The oracle (plain float64 C++, OpenMP) on the host cores: one whole step of the same
-    workload (RoPE on Q and K, forward, analytic backward, inverse RoPE on dQ and dK)."""
-    from oracle import oracle
-    inp = W.make_inputs(w)
+    """The oracle (plain float64 C++, OpenMP) on the host cores, timed as it stands.
+
+    On the headline workload with every available thread: the whole step (RoPE on Q and K,
+    forward, analytic backward, inverse RoPE on dQ and dK) and the forward alone (RoPE and
+    forward).  Then one thread on the three smaller workloads' whole step (the tiny CPU model
+    in full; the GPU-pipeline layer and the T=1024 shape on one (batch, K/V head) slice, scaled
+    by B * Hkv: every slice does the same work).  Inputs are the bench's seeded inputs in
+    float64; generation and conversion are outside the timed calls."""
     import numpy as np
-    arrs = {k: np.ascontiguousarray(v.to(dtype=__import__("torch").float64).numpy())
-            for k, v in inp.items() if k != "peaky"}
-    times = []
-    budget = 30.0
-    t_all = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        qr = oracle.rope(arrs["q_raw"], w.base)
-        kr = oracle.rope(arrs["k_raw"], w.base)
-        oracle.attn_fwd(qr, kr, arrs["v"])
-        dq, dk, _ = oracle.attn_bwd(qr, kr, arrs["v"], arrs["dout"])
-        oracle.rope(dq, w.base, inverse=True)
-        oracle.rope(dk, w.base, inverse=True)
-        times.append(time.perf_counter() - t0)
-        spent = time.perf_counter() - t_all
-        if len(times) >= 3 or spent + times[-1] > budget or spent > 10.0:
-            break
-    t = statistics.median(times)
-    return {"value": round(w.flops_total() / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    import torch
+    from oracle import oracle
+
+    def arrays(wl, b=None, kv=None):
+        inp = W.make_inputs(wl)
+        out = {}
+        for k_, v_ in inp.items():
+            if k_ == "peaky":
+                continue
+            a = v_.to(dtype=torch.float64).numpy()
+            if b is not None:
+                g = wl.Hq // wl.Hkv
+                hs = slice(kv * g, (kv + 1) * g) if v_.shape[2] == wl.Hq else slice(kv, kv + 1)
+                a = a[b:b + 1, :, hs]
+            out[k_] = np.ascontiguousarray(a)
+        return out
+
+    def fwd(wl, a):
+        qr = oracle.rope(a["q_raw"], wl.base)
+        kr = oracle.rope(a["k_raw"], wl.base)
+        oracle.attn_fwd(qr, kr, a["v"])
+        return qr, kr
+
+    def whole(wl, a):
+        qr, kr = fwd(wl, a)
+        dq, dk, _ = oracle.attn_bwd(qr, kr, a["v"], a["dout"])
+        oracle.rope(dq, wl.base, inverse=True)
+        oracle.rope(dk, wl.base, inverse=True)
+
+    def timed(fn, budget=10.0, reps=3):
+        times, t_all = [], time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+            spent = time.perf_counter() - t_all
+            if len(times) >= reps or spent + times[-1] > budget:
+                break
+        return statistics.median(times), len(times)
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    oracle.set_num_threads(threads)
+    cores = oracle.num_threads()
+    a = arrays(w)
+    t_step, n_step = timed(lambda: whole(w, a))
+    t_fwd, n_fwd = timed(lambda: fwd(w, a))
+    single = {}
+    oracle.set_num_threads(1)
+    try:
+        for name in ("tiny_cpu_model", "gpu_model_f32", "blog_t1024"):
+            wl = W.WORKLOADS[name]
+            sliced = name != "tiny_cpu_model"
+            aa = arrays(wl, 0, 0) if sliced else arrays(wl)
+            scale = wl.B * wl.Hkv if sliced else 1
+            ts, _ = timed(lambda: whole(wl, aa), budget=5.0, reps=1)
+            single[name] = {"seconds_per_step": round(ts * scale, 3),
+                            "tflops": round(wl.flops_total() / (ts * scale) / 1e12, 6),
+                            "timed": ("one (batch, K/V head) slice x %d" % scale) if sliced else "whole step"}
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(w.flops_total() / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": "whole step of workload %s (RoPE q/k, fwd, analytic bwd, inverse RoPE), float64, "
-                      "median of %d run(s), %.2f s each" % (w.name, len(times), t),
-            "seconds_per_step": round(t, 3)}
+                      "%d threads, median of %d run(s)" % (w.name, cores, n_step),
+            "seconds_per_step": round(t_step, 3),
+            "forward_only": {"seconds": round(t_fwd, 3), "tflops": round(w.flops_fwd() / t_fwd / 1e12, 6),
+                             "runs": n_fwd, "what": "RoPE on q and k, then the forward"},
+            "single_thread": single}
 
 
 def time_extra(args, torch, ea, W) -> dict:
@@ -444,11 +506,44 @@ def time_extra(args, torch, ea, W) -> dict:
         steps = max(5, args.steps // 5)
         we, _, mse, _, ke = time_workload(name, steps, max(2, args.warmup // 5), torch, ea, W)
         tf = we.flops_total() / (mse * 1e-3) / 1e12
+        dom = max(ke, key=ke.get)
         extra[name] = {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(mse, 4),
                        "frac_of_peak": round(tf / PEAK_TFLOPS[we.dtype], 4), "steps": steps,
                        "config": we.describe(),
-                       "kernel_us": {k: round(v, 2) for k, v in ke.items()}}
+                       "kernel_us": {k: round(v, 2) for k, v in ke.items()},
+                       "roofline": roofline_for(we, ke, dom),
+                       "roofline_attn_fwd": roofline_for(we, ke, "attn_fwd"),
+                       "roofline_attn_bwd_main": roofline_for(we, ke, "attn_bwd_main")}
     return extra
+
+
+def time_cold(name, steps, warmup, torch, ea, W):
+    """The headline step with cold caches: before every step a 512 MiB buffer is written
+    (twice the 256 MB last-level cache of the chip), so the step's inputs come from HBM; HIP
+    events on the launch stream bracket the step alone, not the eviction."""
+    w = W.WORKLOADS[name]
+    log("[bench] cold-cache step, workload %s" % name)
+    inp = W.make_inputs(w)
+    step = Step(w, inp, torch, ea)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step.run()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    tf = w.flops_total() / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+            "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4), "steps": steps,
+            "flush_bytes_between_steps": 512 << 20, "config": w.describe()}
 
 
 def main() -> int:
@@ -472,8 +567,11 @@ def main() -> int:
     ap.add_argument("--proj", default="blog_t1024",
                     help="comma-separated workloads whose QKV / output projections (forward and backward) "
                          "are timed under 'projections'; empty to skip")
+    ap.add_argument("--cold", default="blog_t1024,long_t8192",
+                    help="comma-separated workloads whose step is also timed with cold caches (512 MiB "
+                         "written before every step), reported under 'cold_cache'; empty to skip")
     ap.add_argument("--only", default="",
-                    help="profiling aid: comma-separated subset of extra,decode,projections,noncausal,fwd_rope to run "
+                    help="profiling aid: comma-separated subset of extra,decode,projections,noncausal,fwd_rope,cold to run "
                          "WITHOUT the headline step (prints those sections only, not the benchmark line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (known bytes) five times, for "
@@ -520,6 +618,9 @@ def main() -> int:
             out["noncausal"] = {name: time_noncausal(name, max(5, args.steps // 5), max(2, args.warmup // 5),
                                                      torch, ea, W)
                                 for name in [x for x in args.noncausal.split(",") if x]}
+        if "cold" in want:
+            out["cold_cache"] = {name: time_cold(name, max(10, args.steps // 2), max(2, args.warmup // 5), torch,
+                                                 ea, W) for name in [x for x in args.cold.split(",") if x]}
         if "fwd_rope" in want:
             out["fwd_rope"] = {name: time_fwd_rope(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                                for name in [x for x in args.fwd_rope.split(",") if x]}
@@ -563,6 +664,8 @@ def main() -> int:
                         for name in [x for x in args.noncausal.split(",") if x]}
     out["fwd_rope"] = {name: time_fwd_rope(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)
                        for name in [x for x in args.fwd_rope.split(",") if x]}
+    out["cold_cache"] = {name: time_cold(name, max(10, args.steps // 2), max(2, args.warmup // 5), torch, ea, W)
+                         for name in [x for x in args.cold.split(",") if x]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on host cores")
         out["cpu_baseline"] = cpu_baseline(w, W)

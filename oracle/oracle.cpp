@@ -46,6 +46,10 @@ extern "C" {
 // Number of OpenMP threads a parallel region of this library would use.
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+// Threads for the following parallel regions (a timing aid; no effect on any result, since
+// every sum in this file runs in one thread in a fixed order).
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 // RoPE on x [B, T, H, D] -> y (y may equal x).  For every row (b, t, h) and every pair
 // i in [0, D/2):  theta_i = base^(-2i/D),  phi = (pos0 + t) * theta_i  (negated when
 // inverse != 0), and the pair is rotated by phi:

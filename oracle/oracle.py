@@ -65,6 +65,8 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         L = ctypes.c_long
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_rope.argtypes = [dp, dp, L, L, L, L, ctypes.c_double, L, ctypes.c_int]
         lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_attn_fwd.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double]
@@ -96,6 +98,11 @@ def _ptr(a: np.ndarray):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel regions use (OMP_NUM_THREADS)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP threads of the following calls (timing only; results do not change)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def rope(x, base: float = 10000.0, pos0: int = 0, inverse: bool = False) -> np.ndarray:
