@@ -17,15 +17,21 @@
 //    MFMA tiles: a lane then holds one query column and 16 keys per tile, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two lane halves.
 //    O^T += V^T P^T takes the score registers directly as its B operand.
-//  * K and V tiles are staged row-major in LDS with 16-byte row padding (16-byte operand
-//    reads conflict-free).  K feeds S^T = K Q^T with plain 16-byte reads; V^T, the A operand
-//    of O^T, is read with gfx950's transposing LDS read (ds_read_b64_tr_b16), so no
-//    transposed copy is ever written.  Two LDS buffers: tile j+1 is committed from
+//  * K and V tiles are staged row-major in LDS.  K feeds S^T = K Q^T with plain 16-byte
+//    reads of 16 consecutive rows (16 bytes of row padding keep them on distinct banks); V^T,
+//    the A operand of O^T, is read with gfx950's transposing LDS read (ds_read_b64_tr_b16),
+//    so no transposed copy is ever written, and V rows are padded to a stride of 16 dwords
+//    modulo the 64 banks, which keeps the 4 rows of each transposing read on distinct banks.  Two LDS buffers: tile j+1 is committed from
 //    registers while tile j is computed, and tile j+2 is in flight from HBM; one barrier
 //    per tile.
-//  * The online-softmax rescale is lazy: the running max used for exponentiation is raised
-//    only when a row's max grows by more than 2^8 (then O and l are rescaled), so P stays
-//    below 256 and most tiles skip the rescale; the result is exact either way.
+//  * The online softmax takes P against the running max m without forming each tile's row
+//    max: only a row whose tile sum exceeds 2^16, or is not finite (its first tile, where m is
+//    still -inf), forms the tile max, raises m to it, rescales O and l and takes P again
+//    (from scores formed again: the first tile of a wave pays for its scores twice).  The
+//    result is exact either way; every decision depends only on the row's own scores, and
+//    most tiles skip the max reduction and the exchange of its two lane halves.  Key-split
+//    launches, whose waves see few tiles, instead form every tile's max and raise m lazily,
+//    when a row's max grows by more than 2^8.
 //  * Small problems (too few query blocks to fill the chip twice) split each query block's
 //    key range over KSPL = 2 waves that take alternate K/V tiles; their (max, sum, output)
 //    partials merge exactly through LDS at the end.  This halves the serial work of the
@@ -59,7 +65,8 @@ struct FwdArgs {
     void* q_r;          // ... and the rotated rows are written here
 };
 
-constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest un-normalised P
+constexpr float kSumLimit = 65536.0f;       // largest tile row sum taken against a stale max
+constexpr float kRescaleThreshold = 8.0f;  // key-split launches: log2 of the largest P
 
 template <typename T, int D, int QB, int BN, int NW, int KSPL>
 struct FwdCfg {
@@ -70,15 +77,23 @@ struct FwdCfg {
     static constexpr int PS = 16 / KPL;       // MFMA steps per 32-key block
     static constexpr int EPC = 16 / sizeof(T);
     static constexpr int CPR = D / EPC;       // 16-byte chunks per K/V row
-    static constexpr int KSTR = D + EPC;      // K / V tile row stride (16 bytes of padding)
+    // Row strides (elements) of the K and V tiles.  K is read as 16-byte pieces of 16
+    // consecutive rows: a stride of D + 16 bytes puts those rows on distinct banks.  V is read
+    // only by the transposing read, 4 rows x 64 bytes per 32 lanes: for bf16 a stride that is
+    // 16 dwords modulo the 64 banks puts those 4 rows on distinct banks.
+    static constexpr int KSTR = D + EPC;
+    static constexpr int VSTR = sizeof(T) == 2 ? (D == 32 ? 32 : D + 32) : D + EPC;
+    static_assert(sizeof(T) != 2 || ((VSTR / 2) % 64 == 16 || (VSTR / 2) % 64 == 48), "V stride");
     static constexpr int NT = 64 * NW;
     static constexpr int NCH = (KSPL * BN * CPR + NT - 1) / NT;  // chunks per thread per tensor
     static constexpr int QW = 32 * QB;
     static constexpr int KBUF = BN * KSTR;
+    static constexpr int VBUF = BN * VSTR;
     static constexpr int NBUF = 2 * KSPL;     // double buffer per key split
     // Merge area for the key splits' partials (reuses the K tiles after the loop).
     static constexpr int MERGE_FLOATS = (NW / KSPL) * (16 * (D / 32) * QB + 2 * QB) * 64;
-    static_assert(KSPL == 1 || MERGE_FLOATS * 4 <= (int)(2 * NBUF * KBUF * sizeof(T)), "merge area");
+    static constexpr int LDS_ELEMS = NBUF * (KBUF + VBUF);
+    static_assert(KSPL == 1 || MERGE_FLOATS * 4 <= (int)(LDS_ELEMS * sizeof(T)), "merge area");
 };
 
 template <typename T, int D, int QB, int BN, int NW, int KSPL>
@@ -91,7 +106,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     constexpr int KPL = C::KPL;
 
     // K tiles, then V tiles (one array: the key-split merge reuses both).
-    __shared__ __attribute__((aligned(16))) T KVs[2 * C::NBUF * C::KBUF];
+    __shared__ __attribute__((aligned(16))) T KVs[C::LDS_ELEMS];
     T* const Ks = KVs;
     T* const Vs = KVs + C::NBUF * C::KBUF;
 
@@ -187,9 +202,8 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
             if (u < KSPL * BN * C::CPR) {
                 const int sp = u / (BN * C::CPR), c = u % (BN * C::CPR);
                 const int key = c / C::CPR, part = c % C::CPR;
-                const int o = (sp * 2 + buf) * C::KBUF + key * C::KSTR + part * C::EPC;
-                st16(&Ks[o], kreg[n]);
-                st16(&Vs[o], vreg[n]);
+                st16(&Ks[(sp * 2 + buf) * C::KBUF + key * C::KSTR + part * C::EPC], kreg[n]);
+                st16(&Vs[(sp * 2 + buf) * C::VBUF + key * C::VSTR + part * C::EPC], vreg[n]);
             }
         }
     };
@@ -205,11 +219,8 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     }
 
     // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto compute = [&](int j, int buf, auto masked) {
+    auto scores = [&](const T* kb, int j, f32x16 (&sacc)[QB][C::NKB], auto masked) {
         constexpr bool MASK = decltype(masked)::value;
-        const T* kb = Ks + (ks * 2 + buf) * C::KBUF;
-        const T* vb = Vs + (ks * 2 + buf) * C::KBUF;
-        f32x16 sacc[QB][C::NKB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -223,48 +234,105 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = M::mma(af, qf[qb][s], sacc[qb][kb2]);
             }
         }
+        if constexpr (MASK) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            // Last key this lane's query sees.
-            const int lim = a.causal ? q0 + qb * 32 + l32 : a.T - 1;
-            float mx = -INFINITY;
+            for (int qb = 0; qb < QB; ++qb) {
+                // Last key this lane's query sees.
+                const int lim = a.causal ? q0 + qb * 32 + l32 : a.T - 1;
 #pragma unroll
-            for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
+                for (int kb2 = 0; kb2 < C::NKB; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (MASK) {
-                        const int key = j * BN + kb2 * 32 + acc_row(r, half);
-                        if (key > lim) sacc[qb][kb2][r] = -INFINITY;
-                    }
-                    mx = fmaxf(mx, sacc[qb][kb2][r]);
-                }
+                    for (int r = 0; r < 16; ++r)
+                        if (j * BN + kb2 * 32 + acc_row(r, half) > lim) sacc[qb][kb2][r] = -INFINITY;
             }
-            mx = fmaxf(mx, xor_shfl32(mx)) * a.sl2;
-            // Lazy rescale: raise the running max only when this tile exceeds it by > 2^8.
-            const bool grow = mx > mrun[qb] + kRescaleThreshold;
-            if (__builtin_expect(__any(grow), 0)) {
-                const float mnew = grow ? mx : mrun[qb];
-                const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);  // 0 on the first tile
-                l[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-                mrun[qb] = mnew;
-            }
-            const float mcur = mrun[qb];
-            float rs = 0.0f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[qb][kb2][r] * a.sl2 - mcur);
-                    sacc[qb][kb2][r] = p;
-                    rs += p;
-                }
-            }
-            l[qb] += rs;
         }
+    };
+    // P = exp2(S scale log2(e) - m) in place; returns the row sum of the tile (both halves of
+    // the row, in both lanes), accumulated as four independent partial sums.
+    auto exp_sum = [&](f32x16 (&sv)[C::NKB], float m) {
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < C::NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(sv[kb2][r] * a.sl2 - m);
+                sv[kb2][r] = p;
+                ps[r & 3] += p;
+            }
+        return half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    };
+    // Row max of a tile (both halves of the row), in log2 units.
+    auto tile_max = [&](const f32x16 (&sv)[C::NKB]) {
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kb2 = 0; kb2 < C::NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sv[kb2][r]);
+        return half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * a.sl2;
+    };
+    // Large launches (no key split) take P against the running max first and form the tile
+    // max only where the tile sum calls for it (see the file header).  The key-split launches
+    // of small problems, whose waves see few tiles (the first always needs the max), form the
+    // max of every tile and raise the running max when it grows by more than 2^8.
+    auto compute = [&](int j, int buf, auto masked) {
+        const T* kb = Ks + (ks * 2 + buf) * C::KBUF;
+        const T* vb = Vs + (ks * 2 + buf) * C::VBUF;
+        f32x16 sacc[QB][C::NKB];
+        scores(kb, j, sacc, masked);
+        float rs[QB];
+        bool need[QB];
+        bool any_need = false;
+        if constexpr (KSPL > 1) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mx = tile_max(sacc[qb]);
+                const bool grow = mx > mrun[qb] + kRescaleThreshold;
+                if (__builtin_expect(__any(grow), 0)) {
+                    const float mnew = grow ? mx : mrun[qb];
+                    const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);  // 0 on the first tile
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                    mrun[qb] = mnew;
+                }
+                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
+            }
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
+                need[qb] = !(rs[qb] <= kSumLimit);
+                any_need |= need[qb];
+            }
+        }
+        if (KSPL == 1 && __builtin_expect(__any(any_need), 0)) {
+            // Rows that need it: tile max, new running max, rescale of O and l, P again.
+            // Rows that do not take P again against their unchanged m (the same values).
+            // The scores are formed again from LDS; the empty asm hides the address so that the
+            // compiler reloads the K fragments here instead of keeping the first loads alive
+            // through the common path.
+            const T* kb2p = kb;
+            asm volatile("" : "+v"(kb2p));
+            scores(kb2p, j, sacc, masked);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                if (need[qb]) {
+                    const float mnew = fmaxf(tile_max(sacc[qb]), mrun[qb]);
+                    const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                    mrun[qb] = mnew;
+                }
+                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l[qb] += rs[qb];
 #pragma unroll
         for (int kb2 = 0; kb2 < C::NKB; ++kb2) {
 #pragma unroll
@@ -274,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
                 for (int qb = 0; qb < QB; ++qb) pf[qb] = acc_to_frag<T>(sacc[qb][kb2], ps * KPL);
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const frag vf = load_rows_frag<T>(vb, C::KSTR, kb2 * 32, ps, db * 32);
+                    const frag vf = load_rows_frag<T>(vb, C::VSTR, kb2 * 32, ps, db * 32);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = M::mma(vf, pf[qb], oacc[qb][db]);
                 }
@@ -359,7 +427,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
 
     if constexpr (KSPL == 2) {
         // Merge the two key splits: m = max(m0, m1), a_i = 2^(m_i - m),
-        // l = a0 l0 + a1 l1, O = a0 O0 + a1 O1 (per lane, before the halves combine).
+        // l = a0 l0 + a1 l1, O = a0 O0 + a1 O1 (per lane; l already holds the whole row).
         constexpr int PER = 16 * C::NDB * QB + 2 * QB;
         float* mb = reinterpret_cast<float*>(Ks) + (size_t)slot * PER * 64;
         ostage = reinterpret_cast<T*>(mb);
@@ -410,7 +478,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int tq = q0 + qb * 32 + l32;
-        const float lt = l[qb] + xor_shfl32(l[qb]);
+        const float lt = l[qb];  // both halves of the row already summed
         const float inv = 1.0f / lt;
         if (half == 0 && tq < a.T)
             a.lse[((long long)b * a.Hq + head) * a.T + tq] = (mrun[qb] + __log2f(lt)) * kLn2;

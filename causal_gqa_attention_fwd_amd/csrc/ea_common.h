@@ -197,8 +197,18 @@ __device__ inline f32x16 zero_acc() {
     return z;
 }
 
-__device__ inline float xor_shfl32(float x) {
-    return __shfl_xor(x, 32, 64);
+// Max and sum of x over the lane pair (l, l ^ 32), returned in both lanes: one
+// v_permlane32_swap (the two 32-lane halves exchange x) and one VALU op, no LDS round trip.
+// The swap leaves lane l < 32 with (x[l], x[l + 32]) and lane l >= 32 with (x[l - 32], x[l]),
+// so both lanes of a pair combine the same two values in the same order.
+__device__ inline float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // RoPE frequencies theta_i = base^(-2i/D), i < D/2 <= 128, computed on the host in double
