@@ -274,9 +274,10 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     // max only where the tile sum calls for it (see the file header).  The key-split launches
     // of small problems, whose waves see few tiles (the first always needs the max), form the
     // max of every tile and raise the running max when it grows by more than 2^8.
-    auto compute = [&](int j, int buf, auto masked) {
-        const T* kb = Ks + (ks * 2 + buf) * C::KBUF;
-        const T* vb = Vs + (ks * 2 + buf) * C::VBUF;
+    // slot = 2 * (key split) + buffer.
+    auto compute = [&](int j, int slot, auto masked) {
+        const T* kb = Ks + slot * C::KBUF;
+        const T* vb = Vs + slot * C::VBUF;
         f32x16 sacc[QB][C::NKB];
         scores(kb, j, sacc, masked);
         float rs[QB];
@@ -310,12 +311,12 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
         if (KSPL == 1 && __builtin_expect(__any(any_need), 0)) {
             // Rows that need it: tile max, new running max, rescale of O and l, P again.
             // Rows that do not take P again against their unchanged m (the same values).
-            // The scores are formed again from LDS; the empty asm hides the address so that the
-            // compiler reloads the K fragments here instead of keeping the first loads alive
+            // The scores are formed again from LDS; the empty asm hides the tile's offset so that
+            // the compiler reloads the K fragments here instead of keeping the first loads alive
             // through the common path.
-            const T* kb2p = kb;
-            asm volatile("" : "+v"(kb2p));
-            scores(kb2p, j, sacc, masked);
+            int slot2 = slot;
+            asm volatile("" : "+v"(slot2));
+            scores(Ks + slot2 * C::KBUF, j, sacc, masked);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 if (need[qb]) {
@@ -403,9 +404,9 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
         const int j = st * KSPL + ks;
         if (!active || j > jmax || (a.causal && j * BN > qlast)) return;
         if (j >= jfirst_masked)
-            compute(j, st & 1, std::true_type{});
+            compute(j, ks * 2 + (st & 1), std::true_type{});
         else
-            compute(j, st & 1, std::false_type{});
+            compute(j, ks * 2 + (st & 1), std::false_type{});
     };
     if constexpr (NSET == 2) {
         for (int st = 0; st < nsteps; st += 2) {
