@@ -59,26 +59,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
         return;
     }
     constexpr int EPC = 16 / sizeof(T);
-    constexpr int LPR = D / EPC;  // lanes per row (4 .. 32)
+    constexpr int LPR = D / EPC;       // lanes per row (4 .. 32)
+    constexpr int RPB = 256 / LPR;     // rows per block: consecutive positions of one (b, h)
     const int tid = threadIdx.x;
-    const long long row = (long long)blockIdx.x * (256 / LPR) + tid / LPR;
+    // Block -> (b, h, block of RPB positions), so that the block's D_t values are contiguous
+    // in [B, Hq, T] and each row is read as whole 16-byte chunks.
+    const long long tblocks = (T_ + RPB - 1) / RPB;
+    const long long bh = (long long)blockIdx.x / tblocks;
+    const int t = (int)((long long)blockIdx.x % tblocks) * RPB + tid / LPR;
+    const long long b = bh / Hq, h = bh % Hq;
     const int c = tid % LPR;
+    const bool ok = t < T_ && bh * T_ < nrows;
+    const long long row = (b * T_ + t) * Hq + h;
     float acc = 0.0f;
-    if (row < nrows) {
+    if (ok) {
         const Vec16<T> a = ld16(o + row * D + c * EPC);
         const Vec16<T> d = ld16(dout + row * D + c * EPC);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc += to_f32(a.get(e)) * to_f32(d.get(e));
+        for (int e = 0; e < EPC; ++e) acc = __builtin_fmaf(to_f32(a.get(e)), to_f32(d.get(e)), acc);
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < nrows && c == 0) {
-        const long long h = row % Hq;
-        const long long bt = row / Hq;
-        const long long t = bt % T_;
-        const long long b = bt / T_;
-        dt[(b * Hq + h) * T_ + t] = acc;
-    }
+    if (ok && c == 0) dt[bh * T_ + t] = acc;
 }
 
 constexpr int kMaxOrder = 256;  // items per (batch, K/V head) the dispatch table can hold
@@ -818,7 +820,7 @@ hipError_t launch_pre_t(const void* o, const void* dout, float* dtbuf, int B, in
     const long long nrows = (long long)B * seq * Hq;
     constexpr int LPR = D / (16 / sizeof(T));
     const long long rows_per_block = 256 / LPR;
-    const long long dt_blocks = (nrows + rows_per_block - 1) / rows_per_block;
+    const long long dt_blocks = (long long)B * Hq * ((seq + rows_per_block - 1) / rows_per_block);
     RopeFreq f;
     fill_rope_freq(&f, D, rope ? rope->base : 2.0);
     const long long tab_blocks = rope ? ((long long)seq * (D / 2) + 255) / 256 : 0;

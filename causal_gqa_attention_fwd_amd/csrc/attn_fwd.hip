@@ -173,23 +173,46 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     };
     Stg sa;
     [[maybe_unused]] Stg sb;
+    // Chunk n of this thread: key row tkey (0 .. KSPL * BN - 1 within a step), 16-byte part
+    // tpart; its byte offset from the step's first key row is fixed for the whole loop (when
+    // it fits 32 bits), so a step's loads are a wave-uniform base plus that offset.
+    const long long row_bytes = (long long)a.Hkv * D * sizeof(T);
+    // (Head_dim 128 keeps the per-chunk index arithmetic: its register budget has no room for
+    // the offsets.)
+    const bool off32 = D < 128 && (long long)KSPL * BN * row_bytes < (1LL << 31);
+    // (key row, part) of chunk n; cheap to form again from the thread index where needed.
+    auto chunk_key = [&](int n) { const int u = tid + n * C::NT; return (u / (BN * C::CPR)) * BN + (u % (BN * C::CPR)) / C::CPR; };
+    auto chunk_part = [&](int n) { return (tid + n * C::NT) % C::CPR; };
+    uint32_t toff[C::NCH];
+#pragma unroll
+    for (int n = 0; n < C::NCH; ++n) toff[n] = D < 128 ? (uint32_t)(chunk_key(n) * row_bytes + chunk_part(n) * 16) : 0u;
     auto fetch = [&](Stg& sg, int step) {
         Vec16<T>* kreg = sg.k;
         Vec16<T>* vreg = sg.v;
+        const int s0 = step * KSPL * BN;  // first key of the step
+        if (D < 128 && off32 && s0 + KSPL * BN <= a.T) {
+            const long long base = ((kv_row0 + s0) * a.Hkv + kvh) * D;
+            const char* kb = reinterpret_cast<const char*>(kp + base);
+            const char* vb = reinterpret_cast<const char*>(vp + base);
 #pragma unroll
-        for (int n = 0; n < C::NCH; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < KSPL * BN * C::CPR) {
-                const int sp = u / (BN * C::CPR), c = u % (BN * C::CPR);
-                const int key = c / C::CPR, part = c % C::CPR;
-                const int j = step * KSPL + sp;
-                const int s = j * BN + key;
-                // Keys past the end (or of a tile past jmax, never computed) load a real row
-                // instead: they only occur in a masked tile (the diagonal, or the ragged last
-                // tile without the causal mask), and the loads need no branch.
-                const long long off = ((kv_row0 + min(s, a.T - 1)) * a.Hkv + kvh) * D + part * C::EPC;
-                kreg[n] = ld16(kp + off);
-                vreg[n] = ld16(vp + off);
+            for (int n = 0; n < C::NCH; ++n) {
+                if (tid + n * C::NT < KSPL * BN * C::CPR) {
+                    kreg[n] = ld16(reinterpret_cast<const T*>(kb + toff[n]));
+                    vreg[n] = ld16(reinterpret_cast<const T*>(vb + toff[n]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < C::NCH; ++n) {
+                if (tid + n * C::NT < KSPL * BN * C::CPR) {
+                    // Keys past the end (or of a tile past jmax, never computed) load a real
+                    // row instead: they only occur in a masked tile (the diagonal, or the ragged
+                    // last tile without the causal mask).
+                    const int s = min(s0 + chunk_key(n), a.T - 1);
+                    const long long off = ((kv_row0 + s) * a.Hkv + kvh) * D + chunk_part(n) * C::EPC;
+                    kreg[n] = ld16(kp + off);
+                    vreg[n] = ld16(vp + off);
+                }
             }
         }
     };
@@ -198,10 +221,8 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
         const Vec16<T>* vreg = sg.v;
 #pragma unroll
         for (int n = 0; n < C::NCH; ++n) {
-            const int u = tid + n * C::NT;
-            if (u < KSPL * BN * C::CPR) {
-                const int sp = u / (BN * C::CPR), c = u % (BN * C::CPR);
-                const int key = c / C::CPR, part = c % C::CPR;
+            if (tid + n * C::NT < KSPL * BN * C::CPR) {
+                const int tk = chunk_key(n), sp = tk / BN, key = tk % BN, part = chunk_part(n);
                 st16(&Ks[(sp * 2 + buf) * C::KBUF + key * C::KSTR + part * C::EPC], kreg[n]);
                 st16(&Vs[(sp * 2 + buf) * C::VBUF + key * C::VSTR + part * C::EPC], vreg[n]);
             }
