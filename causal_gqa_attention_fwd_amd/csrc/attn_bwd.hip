@@ -71,15 +71,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
     const int c = tid % LPR;
     const bool ok = t < T_ && bh * T_ < nrows;
     const long long row = (b * T_ + t) * Hq + h;
+    // Chunk dot products, then the DPP lane butterfly of group_sum (no LDS access).
     float acc = 0.0f;
-    if (ok) {
-        const Vec16<T> a = ld16(o + row * D + c * EPC);
-        const Vec16<T> d = ld16(dout + row * D + c * EPC);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc = __builtin_fmaf(to_f32(a.get(e)), to_f32(d.get(e)), acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (ok) acc = dot16(ld16(o + row * D + c * EPC), ld16(dout + row * D + c * EPC));
+    acc = group_sum<LPR>(acc);
     if (ok && c == 0) dt[bh * T_ + t] = acc;
 }
 
@@ -115,6 +110,25 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------------------
 // 2. dK, dV: KV-stationary.
 // ---------------------------------------------------------------------------------------
+// x as a 16-byte chunk (hi, mid, lo, 0, 0, 0, 0, 0) of bf16 with hi = bf16(x), mid =
+// bf16(x - hi), lo = bf16(x - hi - mid) (each difference exact in fp32): hi + mid + lo is x
+// to within 2^-24 |x| or so, which a matrix-core product with (1, 1, 1, 0, ...) adds to an
+// fp32 accumulator.
+template <typename T>
+__device__ inline Vec16<T> pad_parts(float x) {
+    Vec16<T> v = zero16<T>();
+    if constexpr (sizeof(T) == 2) {
+        const T hi = (T)x;
+        const float r1 = x - (float)hi;
+        const T mid = (T)r1;
+        const T lo = (T)(r1 - (float)mid);
+        v.set(0, hi);
+        v.set(1, mid);
+        v.set(2, lo);
+    }
+    return v;
+}
+
 template <typename T, int D, int BM, int QB = 1, int BN_ = 64>
 struct DkdvCfg {
     static constexpr int KPL = Mfma<T>::KPL;
@@ -193,6 +207,21 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         dkacc[db] = zero_acc();
         dvacc[db] = zero_acc();
     }
+    // bf16 head_dim 128: the per-row -LSE/scale and -D ride in the 16-byte padding chunk of
+    // each staged Q and dO row as three bf16 parts (pad_parts), and an extra matrix-core step
+    // multiplies them by this fragment: (1, 1, 1, 0, ...) in the lower half's slots, zero in
+    // the upper half's (whose lanes read the same chunk).  That replaces eight 16-byte LDS
+    // reads per block (the rows' LSE and D, the same for every lane of a half) by two, for two
+    // more matrix-core steps: measured 5.6% faster at head_dim 128 (eight steps per chain),
+    // slower at head_dim 64 (four).
+    constexpr bool FOLD = sizeof(T) == 2 && D >= 128;
+    [[maybe_unused]] frag ones3{};
+    if constexpr (FOLD) {
+        const T one = (T)(half == 0 ? 1.0f : 0.0f);
+        reinterpret_cast<T*>(&ones3)[0] = one;
+        reinterpret_cast<T*>(&ones3)[1] = one;
+        reinterpret_cast<T*>(&ones3)[2] = one;
+    }
 
     // Iterations: every head of the group x every query tile on or below the diagonal (every
     // query tile without the causal mask).
@@ -233,8 +262,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         if (tid < BM) {
             const int t = i * BM + tid;
             const long long ro = ((long long)b * a.Hq + head) * a.T;
-            st.l = (t < a.T) ? a.lse[ro + t] * kLog2e : INFINITY;
-            st.t = (t < a.T) ? a.dt[ro + t] : 0.0f;
+            if constexpr (FOLD) {
+                // -LSE / scale (rows past the end: a finite -2^100, so that P = 0 without an
+                // infinity meeting the zero operands of the padding step).
+                st.l = (t < a.T) ? -a.lse[ro + t] / a.scale : -0x1p100f;
+                st.t = (t < a.T) ? -a.dt[ro + t] : 0.0f;
+            } else {
+                st.l = (t < a.T) ? a.lse[ro + t] * kLog2e : INFINITY;
+                st.t = (t < a.T) ? -a.dt[ro + t] : 0.0f;  // staged negated: the dP accumulator starts from it
+            }
         }
     };
     auto commit = [&](const Stg& st, int stage) {
@@ -253,8 +289,13 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
             }
         }
         if (tid < BM) {
-            reinterpret_cast<float*>(base + C::OFF_LSE)[tid] = st.l;
-            reinterpret_cast<float*>(base + C::OFF_DT)[tid] = st.t;
+            if constexpr (FOLD) {
+                st16(&Qs[tid * C::QS + D], pad_parts<T>(st.l));
+                st16(&dOs[tid * C::QS + D], pad_parts<T>(st.t));
+            } else {
+                reinterpret_cast<float*>(base + C::OFF_LSE)[tid] = st.l;
+                reinterpret_cast<float*>(base + C::OFF_DT)[tid] = st.t;
+            }
         }
     };
 
@@ -265,13 +306,27 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         const T* Qs = reinterpret_cast<const T*>(base + C::OFF_Q);
         const T* dOs = reinterpret_cast<const T*>(base + C::OFF_DO);
         const float* lse2s = reinterpret_cast<const float*>(base + C::OFF_LSE);
-        const float* dts = reinterpret_cast<const float*>(base + C::OFF_DT);
-        // S = Q K^T and dP = dO V^T on this wave's QB 32 x 32 blocks (lanes = keys).
+        const float* ndts = reinterpret_cast<const float*>(base + C::OFF_DT);  // -D per row
+        // S = Q K^T and dP - D = dO V^T - D on this wave's QB 32 x 32 blocks (lanes = keys).
+        // FOLD: one more step per chain multiplies each row's padding chunk (the parts of
+        // -LSE/scale, resp. -D) by (1, 1, 1, 0, ...), so S - LSE/scale and dP - D come out of
+        // the matrix core.  Otherwise the dP accumulator starts from -D of its rows, read from
+        // LDS straight into it (four 16-byte reads per block, rows acc_row(4 r4 + c, half)).
+        // Either way dS = P (dP - D) is one multiply.
         f32x16 sacc[QB], dpacc[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             sacc[qb] = zero_acc();
-            dpacc[qb] = zero_acc();
+            if constexpr (FOLD) {
+                dpacc[qb] = zero_acc();
+            } else {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ndts[qh * C::QW + qb * 32 + 8 * r4 + 4 * half]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dpacc[qb][4 * r4 + c] = d4[c];
+                }
+            }
         }
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
@@ -282,23 +337,33 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
                 dpacc[qb] = M::mma(load_frag<T>(&dOs[ro]), vf[s], dpacc[qb]);
             }
         }
-        // P = exp(S - LSE) (masked where key > query); dS = P (dP - D).
+        if constexpr (FOLD) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int ro = (qh * C::QW + qb * 32 + l32) * C::QS + D;
+                sacc[qb] = M::mma(load_frag<T>(&Qs[ro]), ones3, sacc[qb]);
+                dpacc[qb] = M::mma(load_frag<T>(&dOs[ro]), ones3, dpacc[qb]);
+            }
+        }
+        // P = exp(S - LSE) (masked where key > query); dS = P (dP - D), the second factor
+        // being the dP accumulator itself.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int lq0 = qh * C::QW + qb * 32 + 8 * r4 + 4 * half;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dts[lq0]);
+                [[maybe_unused]] f32x4 l4;
+                if constexpr (!FOLD) l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int r = 4 * r4 + c;
-                    float p = __builtin_amdgcn_exp2f(sacc[qb][r] * a.sl2 - l4[c]);
+                    float p = FOLD ? __builtin_amdgcn_exp2f(sacc[qb][r] * a.sl2)
+                                   : __builtin_amdgcn_exp2f(sacc[qb][r] * a.sl2 - l4[c]);
                     if constexpr (MASK) {
                         if (mykey > i * BM + lq0 + c) p = 0.0f;
                     }
                     sacc[qb][r] = p;
-                    dpacc[qb][r] = p * (dpacc[qb][r] - d4[c]);
+                    dpacc[qb][r] = p * dpacc[qb][r];
                 }
             }
         }
@@ -502,12 +567,13 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     const long long kv_row0 = (long long)b * a.T;
 
     // Q and dO fragments ("split" over head_dim), LSE and D of this lane's query.
+    constexpr int NC = (D / 2) / C::EPC;  // chunks per half row
     frag qf[C::NS], df[C::NS];
     float lse2 = INFINITY, dtv = 0.0f;
     if (active && tq < a.T) {
         const long long off = (((long long)b * a.T + tq) * a.Hq + head) * D + half * (D / 2);
 #pragma unroll
-        for (int c = 0; c < (D / 2) / C::EPC; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const Vec16<T> qv = ld16(qp + off + c * C::EPC);
             const Vec16<T> dv = ld16(dop + off + c * C::EPC);
 #pragma unroll
@@ -578,13 +644,22 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
         constexpr bool MASK = decltype(masked)::value;
         const T* Ks = smem + stage * C::STAGE + u * BN * C::KS;
         const T* Vs = smem + stage * C::STAGE + C::KBUF + u * BN * C::KS;
+        // The dP accumulator starts from -D of the lane's query where registers allow (16 more
+        // live before the products; the twelve-wave and head_dim-128 shapes would spill), so
+        // that dS = P (dP - D) is one multiply; elsewhere D is subtracted afterwards.
+        constexpr bool DINIT = (sizeof(T) == 2 && D <= 64 && NW <= 8) || (sizeof(T) == 4 && D <= 32);
         f32x16 sacc[C::NKB], pacc[C::NKB];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
             sacc[kb] = zero_acc();
-            pacc[kb] = zero_acc();
+            if constexpr (DINIT) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pacc[kb][r] = -dtv;
+            } else {
+                pacc[kb] = zero_acc();
+            }
         }
-        // S^T = K Q^T and dP^T = V dO^T (lanes = queries, registers = keys).
+        // S^T = K Q^T and dP^T (- D) = V dO^T (- D) (lanes = queries, registers = keys).
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
@@ -603,7 +678,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
                 if constexpr (MASK) {
                     if (j * BN + kb * 32 + acc_row(r, half) > lim) p = 0.0f;
                 }
-                pacc[kb][r] = p * (pacc[kb][r] - dtv);
+                pacc[kb][r] = DINIT ? p * pacc[kb][r] : p * (pacc[kb][r] - dtv);
             }
         }
         // dQ^T += K^T dS^T.
@@ -953,9 +1028,19 @@ hipError_t launch_dq_only(const BwdArgs& a, int G, int WPH, hipStream_t stream) 
     }
 }
 
-// roles: 1 = dK/dV, 2 = dQ, 3 = both.  Both roles share one launch when the dK/dV role alone
-// has at most two workgroups per CU (then each role's causal tail overlaps the other's work);
-// otherwise they run as two launches, each with its own workgroup shape.
+// Both roles share one launch when the dK/dV role alone has at most two workgroups per CU
+// (then each role's causal tail overlaps the other's work) and the dQ role's workgroup fits
+// the dK/dV role's wave count.
+template <typename T, int D>
+bool shared_launch(const BwdArgs& a) {
+    int G, WPH;
+    pick_dq_shape<D>(a.Hq / a.Hkv, &G, &WPH);
+    const long long dkdv_blocks = (long long)((a.T + 63) / 64) * a.B * a.Hkv;
+    return dkdv_blocks <= 512 && G * WPH <= dkdv_waves<T, D>();
+}
+
+// roles: 1 = dK/dV, 2 = dQ, 3 = both; both roles in one launch when shared_launch holds,
+// otherwise two launches, each with its own workgroup shape.
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     constexpr int NWK = dkdv_waves<T, D>();
@@ -963,8 +1048,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int roles, hipStream_t stream) {
     pick_dq_shape<D>(a.Hq / a.Hkv, &G, &WPH);
     const long long dkdv_blocks = (long long)((a.T + 63) / 64) * a.B * a.Hkv;
     const bool small = dkdv_blocks <= 512;
-    const bool fuse = roles == 3 && G * WPH <= NWK && small;
-    if (fuse) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
+    if (roles == 3 && shared_launch<T, D>(a)) return launch_bwd_cfg<T, D, NWK>(a, G, WPH, 3, stream);
     if (roles & 1) {
         // The separate dK/dV kernel pays once the 64-key launch would have more than two
         // workgroups per CU; below that the role of the shared launch is used, so that the

@@ -24,14 +24,13 @@
 //    modulo the 64 banks, which keeps the 4 rows of each transposing read on distinct banks.  Two LDS buffers: tile j+1 is committed from
 //    registers while tile j is computed, and tile j+2 is in flight from HBM; one barrier
 //    per tile.
-//  * The online softmax takes P against the running max m without forming each tile's row
-//    max: only a row whose tile sum exceeds 2^16, or is not finite (its first tile, where m is
-//    still -inf), forms the tile max, raises m to it, rescales O and l and takes P again
-//    (from scores formed again: the first tile of a wave pays for its scores twice).  The
-//    result is exact either way; every decision depends only on the row's own scores, and
-//    most tiles skip the max reduction and the exchange of its two lane halves.  Key-split
-//    launches, whose waves see few tiles, instead form every tile's max and raise m lazily,
-//    when a row's max grows by more than 2^8.
+//  * The online softmax forms every tile's row max but raises the running max m (and
+//    rescales O and l) only when a row's max grows by more than 2^8: P is then at most 2^8,
+//    well inside fp32 and bf16 range, and the result is exact either way.  Most tiles skip
+//    the rescale of the output accumulator.  (Taking P against a stale m and forming the max
+//    only where a tile's sum overflows a bound was measured too: on inputs whose logits jump,
+//    such as a workload with a few large key rows, its second pass over the tile costs more
+//    than the max it saves.)
 //  * Small problems (too few query blocks to fill the chip twice) split each query block's
 //    key range over KSPL = 2 waves that take alternate K/V tiles; their (max, sum, output)
 //    partials merge exactly through LDS at the end.  This halves the serial work of the
@@ -65,8 +64,7 @@ struct FwdArgs {
     void* q_r;          // ... and the rotated rows are written here
 };
 
-constexpr float kSumLimit = 65536.0f;       // largest tile row sum taken against a stale max
-constexpr float kRescaleThreshold = 8.0f;  // key-split launches: log2 of the largest P
+constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest P taken against a stale max
 
 template <typename T, int D, int QB, int BN, int NW, int KSPL>
 struct FwdCfg {
@@ -177,20 +175,21 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
     // tpart; its byte offset from the step's first key row is fixed for the whole loop (when
     // it fits 32 bits), so a step's loads are a wave-uniform base plus that offset.
     const long long row_bytes = (long long)a.Hkv * D * sizeof(T);
-    // (Head_dim 128 keeps the per-chunk index arithmetic: its register budget has no room for
-    // the offsets.)
-    const bool off32 = D < 128 && (long long)KSPL * BN * row_bytes < (1LL << 31);
+    // (Head_dim 128 and 64-row waves keep the per-chunk index arithmetic: their register
+    // budgets have no room for the offsets.)
+    constexpr bool HOIST = D < 128 && QB == 1;
+    const bool off32 = HOIST && (long long)KSPL * BN * row_bytes < (1LL << 31);
     // (key row, part) of chunk n; cheap to form again from the thread index where needed.
     auto chunk_key = [&](int n) { const int u = tid + n * C::NT; return (u / (BN * C::CPR)) * BN + (u % (BN * C::CPR)) / C::CPR; };
     auto chunk_part = [&](int n) { return (tid + n * C::NT) % C::CPR; };
     uint32_t toff[C::NCH];
 #pragma unroll
-    for (int n = 0; n < C::NCH; ++n) toff[n] = D < 128 ? (uint32_t)(chunk_key(n) * row_bytes + chunk_part(n) * 16) : 0u;
+    for (int n = 0; n < C::NCH; ++n) toff[n] = HOIST ? (uint32_t)(chunk_key(n) * row_bytes + chunk_part(n) * 16) : 0u;
     auto fetch = [&](Stg& sg, int step) {
         Vec16<T>* kreg = sg.k;
         Vec16<T>* vreg = sg.v;
         const int s0 = step * KSPL * BN;  // first key of the step
-        if (D < 128 && off32 && s0 + KSPL * BN <= a.T) {
+        if (HOIST && off32 && s0 + KSPL * BN <= a.T) {
             const long long base = ((kv_row0 + s0) * a.Hkv + kvh) * D;
             const char* kb = reinterpret_cast<const char*>(kp + base);
             const char* vb = reinterpret_cast<const char*>(vp + base);
@@ -291,10 +290,6 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
             for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sv[kb2][r]);
         return half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * a.sl2;
     };
-    // Large launches (no key split) take P against the running max first and form the tile
-    // max only where the tile sum calls for it (see the file header).  The key-split launches
-    // of small problems, whose waves see few tiles (the first always needs the max), form the
-    // max of every tile and raise the running max when it grows by more than 2^8.
     // slot = 2 * (key split) + buffer.
     auto compute = [&](int j, int slot, auto masked) {
         const T* kb = Ks + slot * C::KBUF;
@@ -302,56 +297,21 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128 && NW == 4) ? 
         f32x16 sacc[QB][C::NKB];
         scores(kb, j, sacc, masked);
         float rs[QB];
-        bool need[QB];
-        bool any_need = false;
-        if constexpr (KSPL > 1) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float mx = tile_max(sacc[qb]);
-                const bool grow = mx > mrun[qb] + kRescaleThreshold;
-                if (__builtin_expect(__any(grow), 0)) {
-                    const float mnew = grow ? mx : mrun[qb];
-                    const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);  // 0 on the first tile
-                    l[qb] *= alpha;
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mx = tile_max(sacc[qb]);
+            const bool grow = mx > mrun[qb] + kRescaleThreshold;
+            if (__builtin_expect(__any(grow), 0)) {
+                const float mnew = grow ? mx : mrun[qb];
+                const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);  // 0 on the first tile
+                l[qb] *= alpha;
 #pragma unroll
-                    for (int db = 0; db < C::NDB; ++db)
+                for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-                    mrun[qb] = mnew;
-                }
-                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
+                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                mrun[qb] = mnew;
             }
-        } else {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
-                need[qb] = !(rs[qb] <= kSumLimit);
-                any_need |= need[qb];
-            }
-        }
-        if (KSPL == 1 && __builtin_expect(__any(any_need), 0)) {
-            // Rows that need it: tile max, new running max, rescale of O and l, P again.
-            // Rows that do not take P again against their unchanged m (the same values).
-            // The scores are formed again from LDS; the empty asm hides the tile's offset so that
-            // the compiler reloads the K fragments here instead of keeping the first loads alive
-            // through the common path.
-            int slot2 = slot;
-            asm volatile("" : "+v"(slot2));
-            scores(Ks + slot2 * C::KBUF, j, sacc, masked);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if (need[qb]) {
-                    const float mnew = fmaxf(tile_max(sacc[qb]), mrun[qb]);
-                    const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
-                    l[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-                    mrun[qb] = mnew;
-                }
-                rs[qb] = exp_sum(sacc[qb], mrun[qb]);
-            }
+            rs[qb] = exp_sum(sacc[qb], mrun[qb]);
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l[qb] += rs[qb];

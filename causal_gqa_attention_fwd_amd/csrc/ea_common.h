@@ -25,6 +25,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace ea {
 
@@ -209,6 +210,37 @@ __device__ inline float half_max(float x) {
 __device__ inline float half_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of x over each aligned group of W lanes (W = 1, 2, 4, ..., 64) as a butterfly: partners
+// one lane apart are added first, then two, four, ...  Every lane of a group ends with the same
+// bits, and so does any code that adds the same W values pairwise in that order, across lanes
+// or within one lane (floating-point addition is commutative).  Up to 16 lanes the exchanges
+// are DPP lane permutations (quad permutes, then the mirror of 8 and of 16 lanes, which after
+// the earlier levels hold the same value as the xor partner), so they cost no LDS access.
+template <int W>
+__device__ inline float group_sum(float x) {
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    if constexpr (W >= 2) x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+    if constexpr (W >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+    if constexpr (W >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (W >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+    if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (W >= 64) x = half_sum(x);
+    return x;
+}
+
+// Dot product of two 16-byte chunks: one fused multiply-add per element, in element order,
+// starting from zero.
+template <typename T>
+__device__ inline float dot16(const Vec16<T>& a, const Vec16<T>& b) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::N; ++e) acc = __builtin_fmaf(to_f32(a.get(e)), to_f32(b.get(e)), acc);
+    return acc;
 }
 
 // RoPE frequencies theta_i = base^(-2i/D), i < D/2 <= 128, computed on the host in double
