@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
     "attn_fwd": ["causal_gqa_attention_fwd_amd/csrc/attn_fwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
-    "attn_bwd": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_bwd_main": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
 }
 
 
@@ -58,7 +58,7 @@ def sources_sha(paths) -> str:
 
 
 class Step:
-    """Preallocated buffers and the three entry-point calls of one step, through the C ABI."""
+    """Preallocated buffers and the five launches of one step, called through the C ABI."""
 
     def __init__(self, w, inp, torch, ea):
         self.w = w
@@ -89,9 +89,11 @@ class Step:
                                           D, dtc, base, 0, 0, stream)),
             ("attn_fwd", L.attn_fwd, (p(self.qr), p(self.kr), p(self.v), p(self.o), p(self.lse), B, T, Hq,
                                       Hkv, D, scale, dtc, stream)),
-            ("attn_bwd", L.attn_bwd_rope, (p(self.qr), p(self.kr), p(self.v), p(self.o), p(self.lse),
-                                           p(self.do), p(self.dq_raw), p(self.dk_raw), p(self.dv), p(self.ws),
-                                           nws, B, T, Hq, Hkv, D, scale, dtc, base, 0, stream)),
+            ("attn_bwd_pre", L.attn_bwd_rope_preprocess, (p(self.o), p(self.do), p(self.ws), nws, B, T, Hq,
+                                                          Hkv, D, dtc, base, 0, stream)),
+            ("attn_bwd_main", L.attn_bwd_rope_main, (p(self.qr), p(self.kr), p(self.v), p(self.lse),
+                                                     p(self.do), p(self.dq_raw), p(self.dk_raw), p(self.dv),
+                                                     p(self.ws), nws, B, T, Hq, Hkv, D, scale, dtc, stream)),
         ]
 
     def run(self):
@@ -118,12 +120,13 @@ def algorithmic(w) -> dict:
     return {
         "rope_qk": {"bytes": 2 * qb + 2 * kb},
         "attn_fwd": {"flops": w.flops_fwd(), "bytes": qb + 2 * kb + qb + lse},
+        # D_t (read O and dO, write D_t) and the RoPE (cos, sin) table, fp32 [T, D/2, 2].
+        "attn_bwd_pre": {"bytes": 2 * qb + lse + w.T * w.D * 4},
         # The backward's 10D per pair (S recompute, dP, dV, dK, dQ); the dQ-role workgroups
         # recompute S and dP once more (4D per pair executed, not counted as algorithmic).
-        # Bytes: Q, O, dO, K, V and LSE read, dQ, dK, dV written; D_t = rowsum(dO * O) and the
-        # inverse RoPE on dQ and dK are formed inside (no extra HBM pass counted).
-        "attn_bwd": {"flops": 10 * w.D * w.pairs, "executed_flops": 14 * w.D * w.pairs,
-                     "bytes": 3 * qb + 2 * kb + lse + qb + 2 * kb},
+        # The inverse RoPE on dQ and dK is applied before their stores (no extra HBM pass).
+        "attn_bwd_main": {"flops": 10 * w.D * w.pairs, "executed_flops": 14 * w.D * w.pairs,
+                          "bytes": 2 * qb + 2 * kb + 2 * lse + qb + 2 * kb},
     }
 
 
@@ -510,7 +513,7 @@ def time_extra(args, torch, ea, W) -> dict:
                        "kernel_us": {k: round(v, 2) for k, v in ke.items()},
                        "roofline": roofline_for(we, ke, dom),
                        "roofline_attn_fwd": roofline_for(we, ke, "attn_fwd"),
-                       "roofline_attn_bwd": roofline_for(we, ke, "attn_bwd")}
+                       "roofline_attn_bwd_main": roofline_for(we, ke, "attn_bwd_main")}
     return extra
 
 
@@ -642,7 +645,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), causal=True,
-                       step="rope_apply_qk,attn_fwd,attn_bwd_rope"),
+                       step="rope_qk,attn_fwd,attn_bwd_rope_preprocess,attn_bwd_rope_main"),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": w.flops_total(),
         "flops_convention": "exact causal: 14*D*B*Hq*T(T+1)/2",
@@ -650,7 +653,7 @@ def main() -> int:
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline_for(w, kern_us, dominant),
         "roofline_attn_fwd": roofline_for(w, kern_us, "attn_fwd"),
-        "roofline_attn_bwd": roofline_for(w, kern_us, "attn_bwd"),
+        "roofline_attn_bwd_main": roofline_for(w, kern_us, "attn_bwd_main"),
     }
     out["extra"] = time_extra(args, torch, ea, W)
     out["decode"] = {name: time_decode(name, max(20, args.steps), max(3, args.warmup // 2), torch, ea, W)

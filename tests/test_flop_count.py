@@ -93,7 +93,7 @@ def test_bench_algorithmic_bytes_and_flops():
     assert a["rope_qk"]["bytes"] == 2 * (q + k)                     # read and write Q and K
     assert a["attn_fwd"]["bytes"] == q + 2 * k + q + lse           # Q, K, V in; O, LSE out
     assert a["attn_fwd"]["flops"] == 4 * 8 * w.pairs
-    assert a["attn_bwd"]["flops"] == 10 * 8 * w.pairs
-    assert a["attn_bwd"]["executed_flops"] == 14 * 8 * w.pairs
-    # Q, K, V, O, dO, LSE in; dQ, dK, dV out.
-    assert a["attn_bwd"]["bytes"] == (q + 2 * k + q + q + lse) + (q + 2 * k)
+    assert a["attn_bwd_main"]["flops"] == 10 * 8 * w.pairs
+    assert a["attn_bwd_main"]["executed_flops"] == 14 * 8 * w.pairs
+    # Q, K, V, dO, LSE, D_t in; dQ, dK, dV out.
+    assert a["attn_bwd_main"]["bytes"] == (q + 2 * k + q + 2 * lse) + (q + 2 * k)
