@@ -158,6 +158,98 @@ struct DkdvCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+// End of a dK/dV item: sum the dK/dV partials of the NQH query-block waves of each key block
+// in LDS and store dK, dV.  Wave w holds key block kh = w % NKH, query block qh = w / NKH.
+template <typename T, int D, int NKH, int NQH, int BN, int NT>
+__device__ __forceinline__ void dkdv_epilogue(const BwdArgs& a, char* smem, f32x16 (&dkacc)[D / 32],
+                                              f32x16 (&dvacc)[D / 32], int j, int kvh, int b) {
+    constexpr int NDB = D / 32;
+    constexpr int EPC = 16 / sizeof(T);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int kh = w % NKH;
+    const int qh = w / NKH;
+    // Sum the dK/dV partials of the query blocks in LDS, last block first (fixed order:
+    // deterministic).  The waves of query block 0 then hold the totals; they write them back
+    // row-major per key half ([dK | dV][32 keys][D] floats, dK scaled by `scale`), and every
+    // thread stores 16-byte row segments, with the inverse RoPE of dK applied pair by pair.
+    float* red = reinterpret_cast<float*>(smem);
+    const size_t rbase = (size_t)kh * 2 * NDB * 16 * 64;
+    for (int o = NQH - 1; o >= 0; --o) {
+        __syncthreads();
+        if (qh == o) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const size_t ik = rbase + (size_t)db * 1024 + r * 64 + lane;
+                    const size_t iv = ik + (size_t)NDB * 1024;
+                    if (o < NQH - 1) {
+                        dkacc[db][r] += red[ik];
+                        dvacc[db][r] += red[iv];
+                    }
+                    if (o > 0) {
+                        red[ik] = dkacc[db][r];
+                        red[iv] = dvacc[db][r];
+                    }
+                }
+        }
+    }
+    __syncthreads();  // every partial read
+    if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const size_t at = rbase + (size_t)acc_row(r, half) * D + db * 32 + l32;
+                red[at] = dkacc[db][r] * a.scale;
+                red[at + 32 * D] = dvacc[db][r];
+            }
+    }
+    __syncthreads();
+    constexpr int CPRo = D / EPC;       // 16-byte output chunks per row
+    constexpr int NCHO = 2 * BN * CPRo;    // chunks of dK and dV
+    T* __restrict__ dkp = static_cast<T*>(a.dk);
+    T* __restrict__ dvp = static_cast<T*>(a.dv);
+    for (int c = tid; c < NCHO; c += NT) {
+        const int tsel = c / (BN * CPRo);
+        const int cc = c % (BN * CPRo);
+        const int kl = cc / CPRo, part = cc % CPRo;
+        const int key = j * BN + kl;
+        if (key >= a.T) continue;
+        const float* src = red + (size_t)(kl >> 5) * 2 * NDB * 1024 + (size_t)tsel * 32 * D +
+                           (size_t)(kl & 31) * D + part * EPC;
+        float x[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + e);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[e + u] = v4[u];
+        }
+        if (tsel == 0 && a.rope_cs != nullptr) {
+            // dK_raw = R(-phi) dK on each pair (2p, 2p + 1) of the chunk.
+            const float* tab = a.rope_cs + ((long long)key * (D / 2) + part * (EPC / 2)) * 2;
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4) {
+                const f32x4 w = *reinterpret_cast<const f32x4*>(tab + e);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const float x0 = x[e + 2 * u], x1 = x[e + 2 * u + 1];
+                    rope_rotate(x0, x1, w[2 * u], -w[2 * u + 1], &x[e + 2 * u], &x[e + 2 * u + 1]);
+                }
+            }
+        }
+        Vec16<T> out;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) out.set(e, from_f32<T>(x[e]));
+        T* dst = (tsel == 0 ? dkp : dvp) + (((long long)b * a.T + key) * a.Hkv + kvh) * D + part * EPC;
+        st16(dst, out);
+    }
+}
+
 // One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.  Each wave takes
 // 32 keys and QB blocks of 32 query rows per iteration; with QB = 2 the two blocks' products
 // and exponentials are independent chains that the scheduler interleaves.
@@ -428,82 +520,321 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, char* smem, int j, i
         for (int it = 0; it < niter; ++it) iteration(it, sa);
     }
 
-    // Sum the dK/dV partials of the query blocks in LDS, last block first (fixed order:
-    // deterministic).  The waves of query block 0 then hold the totals; they write them back
-    // row-major per key half ([dK | dV][32 keys][D] floats, dK scaled by `scale`), and every
-    // thread stores 16-byte row segments, with the inverse RoPE of dK applied pair by pair.
-    float* red = reinterpret_cast<float*>(smem);
-    const size_t rbase = (size_t)kh * 2 * C::NDB * 16 * 64;
-    for (int o = C::NQH - 1; o >= 0; --o) {
-        __syncthreads();
-        if (qh == o) {
+    dkdv_epilogue<T, D, C::NKH, C::NQH, BN, C::NT>(a, smem, dkacc, dvacc, j, kvh, b);
+}
+
+// ---------------------------------------------------------------------------------------
+// 2b. dK, dV for bf16 head_dim 64: Q / dO stages copied HBM -> LDS by the load unit.
+// ---------------------------------------------------------------------------------------
+// The same item as dkdv_role, but each stage of Q and dO rows goes from global memory straight
+// into LDS (global_load_lds_dwordx4: each instruction fills 1 KB, lane l at byte 16 l) with no
+// register staging and no LDS stores of those rows.  Rows are 128 bytes, unpadded, with their
+// 16-byte chunks permuted by swz64 so that both kinds of read are free of bank conflicts:
+//  * the 16-byte "split" reads (lanes 0-15: the same logical chunk of 16 consecutive rows)
+//    land on 16 distinct 16-byte bank groups;
+//  * the transposing reads (32 lanes: 4 consecutive rows x 64 bytes) land on 4 distinct
+//    64-byte bank groups.
+// LSE (times log2 e) and -D of a stage go through registers: loaded by every thread in the
+// iteration that issues the stage's copies, stored to LDS by the first BM threads at its end.
+// The compiler's wait for those loads is a wait for every vector-memory operation (it does not
+// count the copies into LDS as later operations), so a stage's copies have one compute phase
+// to land, as with register staging: NST = 2 buffers suffice.  The waits before the barriers
+// are explicit (the compiler's own would be placed at every LDS access).
+
+// Stored chunk of logical chunk c in row r is c ^ swz64(r) (a permutation of bits 1-3 of r).
+__device__ __host__ constexpr inline int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BM, int QB, int BN_, int NST_>
+struct DkdvDmaCfg {
+    static constexpr int D = 64;
+    static constexpr int NST = NST_;
+    static constexpr int BN = BN_;
+    static constexpr int NKH = BN / 32;
+    static constexpr int QW = 32 * QB;
+    static constexpr int NQH = BM / QW;
+    static constexpr int NW = NKH * NQH;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NS = 4;      // MFMA steps over head_dim
+    static constexpr int NDB = 2;
+    static constexpr int TILE = BM * 128;
+    static constexpr size_t OFF_Q = 0;
+    static constexpr size_t OFF_DO = TILE;
+    static constexpr size_t OFF_LSE = 2 * (size_t)TILE;
+    static constexpr size_t OFF_DT = OFF_LSE + sizeof(float) * BM;
+    static constexpr size_t STAGE = OFF_DT + sizeof(float) * BM;
+    static constexpr size_t BYTES = NST * STAGE;
+    static constexpr int NPIECE = BM / 8;          // 1 KB copies per tile
+    static constexpr int PPW = NPIECE / NW;        // copies per wave per tile
+    static constexpr size_t RED_BYTES = (size_t)NKH * 2 * NDB * 16 * 64 * sizeof(float);
+    static_assert(NPIECE % NW == 0, "every wave issues the same number of copies");
+    static_assert(STAGE % 16 == 0, "stage alignment");
+    static_assert(RED_BYTES <= BYTES, "reduction buffer must fit in the staging region");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier: this wave's vector-memory operations but the
+// last N have completed (its copies into LDS included), and so have its LDS accesses.  Written
+// as one asm statement so that no memory access moves across it.
+template <int N>
+__device__ inline void vm_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Operand fragment from two transposing reads (rows r .. r+3, then r+8 .. r+11).
+__device__ inline bf16x8 tr_join(i16x4 x, i16x4 y) {
+    bf16x8 f;
+    const bf16x4 a = __builtin_bit_cast(bf16x4, x);
+    const bf16x4 c = __builtin_bit_cast(bf16x4, y);
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = c[0]; f[5] = c[1]; f[6] = c[2]; f[7] = c[3];
+    return f;
+}
+
+// The transposing reads of one 16-row step of a 32-row block, for both head_dim halves of Q
+// (at LDS byte addresses lo[db] / hi[db]) and of dO (OFF bytes further): eight reads in one asm
+// statement that also waits for them.  (Issued through the builtin, each transposing read makes
+// the compiler wait for every copy into LDS still in flight, the later stages' included; here
+// the wait covers LDS accesses only.)
+template <int OFF>
+__device__ inline void tr_reads8(const unsigned (&lo)[2], const unsigned (&hi)[2], bf16x8 (&qt)[2], bf16x8 (&dt)[2]) {
+    i16x4 q0, q1, q2, q3, d0, d1, d2, d3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+        : "v"(lo[0]), "v"(hi[0]), "v"(lo[1]), "v"(hi[1]), "n"(OFF)
+        : "memory");
+    qt[0] = tr_join(q0, q1);
+    qt[1] = tr_join(q2, q3);
+    dt[0] = tr_join(d0, d1);
+    dt[1] = tr_join(d2, d3);
+}
+
+template <int BM, int QB, int BN_, int NST>
+__device__ __forceinline__ void dkdv_role_dma(const BwdArgs& a, char* smem, int j, int kvh, int b) {
+    using C = DkdvDmaCfg<BM, QB, BN_, NST>;
+    using T = bf16;
+    using M = Mfma<T>;
+    using frag = typename M::frag;
+    constexpr int D = 64;
+    constexpr int KPL = 8;
+    constexpr int BN = C::BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int kh = w % C::NKH;
+    const int qh = w / C::NKH;
+    const int g = a.Hq / a.Hkv;
+
+    const T* __restrict__ qp = static_cast<const T*>(a.q);
+    const T* __restrict__ kp = static_cast<const T*>(a.k);
+    const T* __restrict__ vp = static_cast<const T*>(a.v);
+    const T* __restrict__ dop = static_cast<const T*>(a.dout);
+
+    // Stationary K_j / V_j fragments ("split" over head_dim) for this wave's 32 keys.
+    const int mykey = j * BN + kh * 32 + l32;
+    frag kf[C::NS], vf[C::NS];
+    {
+        const bool ok = mykey < a.T;
+        const long long off = (((long long)b * a.T + mykey) * a.Hkv + kvh) * D + half * (D / 2);
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const size_t ik = rbase + (size_t)db * 1024 + r * 64 + lane;
-                    const size_t iv = ik + (size_t)C::NDB * 1024;
-                    if (o < C::NQH - 1) {
-                        dkacc[db][r] += red[ik];
-                        dvacc[db][r] += red[iv];
-                    }
-                    if (o > 0) {
-                        red[ik] = dkacc[db][r];
-                        red[iv] = dvacc[db][r];
-                    }
-                }
+        for (int c = 0; c < 4; ++c) {
+            const Vec16<T> kv = ok ? ld16(kp + off + c * 8) : zero16<T>();
+            const Vec16<T> vv = ok ? ld16(vp + off + c * 8) : zero16<T>();
+            kf[c] = reinterpret_cast<const frag*>(&kv.raw)[0];
+            vf[c] = reinterpret_cast<const frag*>(&vv.raw)[0];
         }
     }
-    __syncthreads();  // every partial read
-    if (qh == 0) {
+    f32x16 dkacc[C::NDB], dvacc[C::NDB];
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < C::NDB; ++db) {
+        dkacc[db] = zero_acc();
+        dvacc[db] = zero_acc();
+    }
+
+    const int i0 = a.causal ? (j * BN) / BM : 0;
+    const int nq = a.ntq - i0;
+    const int niter = g * nq;
+
+    // Copies of stage it into buffer buf (this wave's PPW pieces of Q and of dO): piece n covers
+    // rows 8n .. 8n+7; lane l fills row 8n + l/8, stored chunk l%8, i.e. logical chunk
+    // (l%8) ^ swz64(row).  Rows past the end copy row T-1 instead (their P is 0: LSE = +inf).
+    auto dma = [&](int it, int buf) {
+        const int head = kvh * g + it / nq;
+        const int i = i0 + it % nq;
+        char* base = smem + buf * C::STAGE;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const size_t at = rbase + (size_t)acc_row(r, half) * D + db * 32 + l32;
-                red[at] = dkacc[db][r] * a.scale;
-                red[at + 32 * D] = dvacc[db][r];
+        for (int u = 0; u < C::PPW; ++u) {
+            const int n = w * C::PPW + u;
+            const int row = 8 * n + (lane >> 3);
+            const int c = (lane & 7) ^ swz64(row);
+            const int t = min(i * BM + row, a.T - 1);
+            const long long off = (((long long)b * a.T + t) * a.Hq + head) * D + c * 8;
+            __builtin_amdgcn_global_load_lds(qp + off, (lds_void*)(base + C::OFF_Q + n * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dop + off, (lds_void*)(base + C::OFF_DO + n * 1024), 16, 0, 0);
+        }
+    };
+    // LSE and D of the stage's rows, loaded raw by every thread (row tid % BM) and stored by the
+    // first BM threads as LSE * log2(e) and -D (+inf and 0 past the end).  The loads and copies
+    // of a stage are issued unconditionally (past the last stage, the last one is copied again
+    // into the free buffer), so that every iteration runs the same straight-line sequence.
+    auto fetch_ld = [&](int it, float& l, float& d) {
+        const int head = kvh * g + it / nq;
+        const int t = min((i0 + it % nq) * BM + (tid % BM), a.T - 1);
+        const long long ro = ((long long)b * a.Hq + head) * a.T;
+        l = a.lse[ro + t];
+        d = a.dt[ro + t];
+    };
+    // (The two LDS stores are written in asm: for an LDS store it can see, the compiler would
+    // first wait for every copy into LDS in flight.)
+    auto commit_ld = [&](int it, int buf, float l, float d) {
+        if (tid < BM) {
+            const bool in = (i0 + it % nq) * BM + tid < a.T;
+            const float lv = in ? l * kLog2e : INFINITY;
+            const float dv = in ? -d : 0.0f;
+            const unsigned at = (unsigned)(uintptr_t)(smem + buf * C::STAGE + C::OFF_LSE) + 4 * tid;
+            asm volatile("ds_write_b32 %0, %1\n\tds_write_b32 %0, %2 offset:%3" ::"v"(at), "v"(lv), "v"(dv),
+                         "n"(4 * BM)
+                         : "memory");
+        }
+    };
+
+    // Lane offsets of the reads.  Split: row l32 of a 32-row block, logical chunk 4 half + s.
+    // Transposing: rows 4 half + (jj >> 2) (and + 8) of a 16-row block, logical chunk
+    // 4 db + 2 grp + ((jj >> 1) & 1), byte 8 (jj & 1) of it.
+    int soff[C::NS];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) soff[s] = l32 * 128 + (((4 * half + s) ^ swz64(l32)) << 4);
+    unsigned tlo[C::NDB], thi[C::NDB];
+    {
+        const int jj = lane & 15, grp = (lane >> 4) & 1;
+        const int r = 4 * half + (jj >> 2);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+            const int c = 4 * db + 2 * grp + ((jj >> 1) & 1);
+            tlo[db] = r * 128 + ((c ^ swz64(r)) << 4) + 8 * (jj & 1);
+            thi[db] = (r + 8) * 128 + ((c ^ swz64(r + 8)) << 4) + 8 * (jj & 1);
+        }
+    }
+
+    auto compute = [&](int it, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        const int i = i0 + it % nq;
+        const char* base = smem + (it % NST) * C::STAGE;
+        const char* qb0 = base + C::OFF_Q + (size_t)qh * C::QW * 128;  // this wave's first row
+        const float* lse2s = reinterpret_cast<const float*>(base + C::OFF_LSE);
+        const float* ndts = reinterpret_cast<const float*>(base + C::OFF_DT);
+        f32x16 sacc[QB], dpacc[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            sacc[qb] = zero_acc();
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ndts[qh * C::QW + qb * 32 + 8 * r4 + 4 * half]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dpacc[qb][4 * r4 + c] = d4[c];
             }
-    }
-    __syncthreads();
-    constexpr int CPRo = D / C::EPC;       // 16-byte output chunks per row
-    constexpr int NCHO = 2 * BN * CPRo;    // chunks of dK and dV
-    T* __restrict__ dkp = static_cast<T*>(a.dk);
-    T* __restrict__ dvp = static_cast<T*>(a.dv);
-    for (int c = tid; c < NCHO; c += C::NT) {
-        const int tsel = c / (BN * CPRo);
-        const int cc = c % (BN * CPRo);
-        const int kl = cc / CPRo, part = cc % CPRo;
-        const int key = j * BN + kl;
-        if (key >= a.T) continue;
-        const float* src = red + (size_t)(kl >> 5) * 2 * C::NDB * 1024 + (size_t)tsel * 32 * D +
-                           (size_t)(kl & 31) * D + part * C::EPC;
-        float x[C::EPC];
-#pragma unroll
-        for (int e = 0; e < C::EPC; e += 4) {
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + e);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x[e + u] = v4[u];
         }
-        if (tsel == 0 && a.rope_cs != nullptr) {
-            // dK_raw = R(-phi) dK on each pair (2p, 2p + 1) of the chunk.
-            const float* tab = a.rope_cs + ((long long)key * (D / 2) + part * (C::EPC / 2)) * 2;
 #pragma unroll
-            for (int e = 0; e < C::EPC; e += 4) {
-                const f32x4 w = *reinterpret_cast<const f32x4*>(tab + e);
+        for (int s = 0; s < C::NS; ++s) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const float x0 = x[e + 2 * u], x1 = x[e + 2 * u + 1];
-                    rope_rotate(x0, x1, w[2 * u], -w[2 * u + 1], &x[e + 2 * u], &x[e + 2 * u + 1]);
+            for (int qb = 0; qb < QB; ++qb) {
+                const char* p = qb0 + qb * 32 * 128 + soff[s];
+                sacc[qb] = M::mma(*reinterpret_cast<const frag*>(p), kf[s], sacc[qb]);
+                dpacc[qb] = M::mma(*reinterpret_cast<const frag*>(p + C::TILE), vf[s], dpacc[qb]);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int lq0 = qh * C::QW + qb * 32 + 8 * r4 + 4 * half;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[lq0]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * r4 + c;
+                    float p = __builtin_amdgcn_exp2f(sacc[qb][r] * a.sl2 - l4[c]);
+                    if constexpr (MASK) {
+                        if (mykey > i * BM + lq0 + c) p = 0.0f;
+                    }
+                    sacc[qb][r] = p;
+                    dpacc[qb][r] = p * dpacc[qb][r];
                 }
             }
         }
-        Vec16<T> out;
 #pragma unroll
-        for (int e = 0; e < C::EPC; ++e) out.set(e, from_f32<T>(x[e]));
-        T* dst = (tsel == 0 ? dkp : dvp) + (((long long)b * a.T + key) * a.Hkv + kvh) * D + part * C::EPC;
-        st16(dst, out);
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) {
+                const frag pf = acc_to_frag<T>(sacc[qb], ps * KPL);
+                const frag dsf = acc_to_frag<T>(dpacc[qb], ps * KPL);
+                const unsigned rb = (unsigned)(uintptr_t)(qb0 + (qb * 32 + 16 * ps) * 128);
+                const unsigned lo[2] = {rb + tlo[0], rb + tlo[1]};
+                const unsigned hi[2] = {rb + thi[0], rb + thi[1]};
+                frag qt[2], dt[2];
+                tr_reads8<C::TILE>(lo, hi, qt, dt);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    dvacc[db] = M::mma(pf, dt[db], dvacc[db]);
+                    dkacc[db] = M::mma(dsf, qt[db], dkacc[db]);
+                }
+            }
+        }
+    };
+
+    if (niter <= 0) {
+        dkdv_epilogue<T, D, C::NKH, C::NQH, BN, C::NT>(a, smem, dkacc, dvacc, j, kvh, b);
+        return;
     }
+    // Prologue: stage 0.
+    static_assert(NST == 2, "the loop below is written for two stages");
+    {
+        float l0, d0;
+        fetch_ld(0, l0, d0);
+        dma(0, 0);
+        commit_ld(0, 0, l0, d0);
+    }
+    // The K_j / V_j loads were issued first; wait for them here, once.
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        settle(kf[s]);
+        settle(vf[s]);
+    }
+    for (int it = 0; it < niter; ++it) {
+        // This wave's copies of stage it complete, then the barrier: every wave's copies of
+        // stage it have landed, and every wave is done with iteration it - 1, whose buffer the
+        // copies of stage it + 1 refill.
+        vm_wait_barrier<0>();
+        const int nx = min(it + 1, niter - 1);
+        const int nbuf = (it + 1) % NST;
+        float lreg, dreg;
+        fetch_ld(nx, lreg, dreg);
+        dma(nx, nbuf);
+        const int i = i0 + it % nq;
+        const int kfirst = j * BN + kh * 32, qfirst = i * BM + qh * C::QW;
+        if (!(a.causal && kfirst > qfirst + C::QW - 1)) {
+            if (a.causal && kfirst + 31 > qfirst)
+                compute(it, std::true_type{});
+            else
+                compute(it, std::false_type{});
+        }
+        commit_ld(nx, nbuf, lreg, dreg);
+    }
+    // The copies of the repeated last stage may still be in flight: the reduction reuses the LDS.
+    vm_wait_barrier<0>();
+    dkdv_epilogue<T, D, C::NKH, C::NQH, BN, C::NT>(a, smem, dkacc, dvacc, j, kvh, b);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -798,15 +1129,27 @@ __device__ inline int dkdv_rank(int j, const Sched& s) {  // merged position of 
     return j + (int)(((long long)j * s.nqi + s.ntk - 1) / s.ntk);
 }
 
+// bf16 head_dim 64 takes the dK/dV role with direct copies into LDS (dkdv_role_dma).
+template <typename T, int D>
+constexpr bool kDkdvDma = sizeof(T) == 2 && D == 64;
+// One 32-row query block per wave in the shared launch (two, over 256-row stages, measured
+// slower at T=1024); two LDS stages (three measured 1-2% slower).
+constexpr int kDmaQbShared = 1;      // query blocks per wave, shared launch
+constexpr int kDmaStagesShared = 2;  // LDS stages of the shared launch's dK/dV role
+constexpr int kDmaStagesSolo = 2;    // and of the separate dK/dV kernel
+
 template <typename T, int D, int NW>
 struct BwdKernelCfg {
-    static constexpr int BM = 16 * NW;  // dK/dV role: 2 key halves x NW/2 query blocks
+    // dK/dV role: 2 key halves x NW/2 query blocks of 32 (or 64) rows
+    static constexpr int BM = (kDkdvDma<T, D> ? 16 * kDmaQbShared : 16) * NW;
     static constexpr int BNQ = (D == 128) ? 32 : 64;  // dQ role key tile
-    using Dk = DkdvCfg<T, D, BM>;
+    using Dk = DkdvCfg<T, D, 16 * NW>;
     using Dq = DqCfg<T, D, BNQ, NW>;
     static constexpr size_t DQ_BYTES = 2 * (size_t)Dq::STAGE * sizeof(T);
-    static constexpr size_t BYTES = Dk::BYTES > DQ_BYTES ? Dk::BYTES : DQ_BYTES;
+    static constexpr size_t DK_BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<BM, kDmaQbShared, 64, kDmaStagesShared>::BYTES : Dk::BYTES;
+    static constexpr size_t BYTES = DK_BYTES > DQ_BYTES ? DK_BYTES : DQ_BYTES;
     static_assert(Dk::NW == NW, "dK/dV role must use every wave");
+    static_assert(!kDkdvDma<T, D> || DkdvDmaCfg<BM, kDmaQbShared, 64, kDmaStagesShared>::NW == NW, "waves");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -844,9 +1187,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_kernel(BwdArgs a) {
         is_dkdv = dkdv_rank(lo, sc) == m;
         item = is_dkdv ? lo : m - (lo + 1);
     }
-    if (is_dkdv)
-        dkdv_role<T, D, K::BM>(a, smem, item, kvh, b);
-    else
+    if (is_dkdv) {
+        if constexpr (kDkdvDma<T, D>)
+            dkdv_role_dma<K::BM, kDmaQbShared, 64, kDmaStagesShared>(a, smem, item, kvh, b);
+        else
+            dkdv_role<T, D, K::BM>(a, smem, item, kvh, b);
+    } else
         dq_role<T, D, K::BNQ, NW>(a, smem, item, kvh, b);
 }
 
@@ -878,15 +1224,19 @@ struct DkdvSolo {
     static constexpr int BN = D <= 64 ? 128 : 64;
     using Cfg = DkdvCfg<T, D, 128, 2, BN>;
     static constexpr int NT = 64 * Cfg::NW;
+    static constexpr size_t BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<128, 2, BN, kDmaStagesSolo>::BYTES : Cfg::BYTES;
 };
 template <typename T, int D>
 __global__ __launch_bounds__((DkdvSolo<T, D>::NT), 1) void bwd_dkdv_kernel(BwdArgs a) {
     using S = DkdvSolo<T, D>;
-    __shared__ __attribute__((aligned(16))) char smem[S::Cfg::BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
     const int HB = a.B * a.Hkv;
     const int m = blockIdx.x / HB;
     const int rem = blockIdx.x % HB;
-    dkdv_role<T, D, 128, 2, S::BN>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+    if constexpr (kDkdvDma<T, D>)
+        dkdv_role_dma<128, 2, S::BN, kDmaStagesSolo>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
+    else
+        dkdv_role<T, D, 128, 2, S::BN>(a, smem, m, rem % a.Hkv, rem / a.Hkv);
 }
 
 template <typename T, int D>
