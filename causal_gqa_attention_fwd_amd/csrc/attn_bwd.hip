@@ -129,6 +129,15 @@ __device__ inline Vec16<T> pad_parts(float x) {
     return v;
 }
 
+// LDS of the dK/dV epilogue's partials (see dkdv_epilogue).
+template <int D>
+constexpr int kEpiStride = D + 4;  // floats per partial row (conflict-free 16-byte reads)
+template <int D, int NKH, int NQH>
+constexpr size_t dkdv_epi_bytes() {
+    return D <= 64 ? (size_t)NQH * NKH * 2 * 32 * kEpiStride<D> * sizeof(float)
+                   : (size_t)NKH * 2 * (D / 32) * 16 * 64 * sizeof(float);
+}
+
 template <typename T, int D, int BM, int QB = 1, int BN_ = 64>
 struct DkdvCfg {
     static constexpr int KPL = Mfma<T>::KPL;
@@ -152,16 +161,112 @@ struct DkdvCfg {
     static constexpr size_t OFF_DT = OFF_LSE + sizeof(float) * BM;
     static constexpr size_t STAGE = (OFF_DT + sizeof(float) * BM + 15) & ~(size_t)15;
     static constexpr size_t BYTES = 2 * STAGE;
-    // One set of dK/dV partials (all key halves) for the final reduction over query blocks.
-    static constexpr size_t RED_BYTES = (size_t)NKH * 2 * NDB * 16 * 64 * sizeof(float);
-    static_assert(RED_BYTES <= BYTES, "reduction buffer must fit in the staging region");
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    // LDS of a workgroup of this role: its stages, or the partials of its epilogue.
+    static constexpr size_t LDS = BYTES > dkdv_epi_bytes<D, NKH, NQH>() ? BYTES : dkdv_epi_bytes<D, NKH, NQH>();
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// End of a dK/dV item: sum the dK/dV partials of the NQH query-block waves of each key block
-// in LDS and store dK, dV.  Wave w holds key block kh = w % NKH, query block qh = w / NKH.
+// End of a dK/dV item (up to head_dim 64).  Every wave writes its dK / dV partial (its 32 keys, the query rows it
+// took) to LDS row-major, [query block][key block][dK | dV][32 keys][D + 4] floats; then every
+// thread takes 16-byte output row segments: it sums the NQH partials of its segment, last
+// query block first (fixed order: deterministic), scales dK, applies the inverse RoPE to dK
+// with (cos, sin) loaded before the partials were written, and stores.  Wave w holds key block
+// kh = w % NKH, query block qh = w / NKH.
+
 template <typename T, int D, int NKH, int NQH, int BN, int NT>
-__device__ __forceinline__ void dkdv_epilogue(const BwdArgs& a, char* smem, f32x16 (&dkacc)[D / 32],
+__device__ __forceinline__ void dkdv_epilogue_all(const BwdArgs& a, char* smem, f32x16 (&dkacc)[D / 32],
+                                              f32x16 (&dvacc)[D / 32], int j, int kvh, int b) {
+    constexpr int NDB = D / 32;
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int PS = kEpiStride<D>;
+    constexpr int CPRo = D / EPC;          // 16-byte output chunks per row
+    constexpr int NCK = BN * CPRo;         // chunks of dK (and of dV)
+    constexpr int NDK = (NCK + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int kh = w % NKH;
+    const int qh = w / NKH;
+    float* part = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the stages in LDS
+    {
+        float* mine = part + (size_t)(qh * NKH + kh) * 2 * 32 * PS;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int at = acc_row(r, half) * PS + db * 32 + l32;
+                mine[at] = dkacc[db][r];
+                mine[32 * PS + at] = dvacc[db][r];
+            }
+    }
+    // (cos, sin) of this thread's dK segments: issued once the accumulators are in LDS, in
+    // flight across the barrier.
+    f32x4 tab[NDK][EPC / 4];
+    if (a.rope_cs != nullptr) {
+#pragma unroll
+        for (int u = 0; u < NDK; ++u) {
+            const int c = tid + u * NT;
+            const int key = min(j * BN + (c < NCK ? c : 0) / CPRo, a.T - 1);
+            const f32x4* src = reinterpret_cast<const f32x4*>(a.rope_cs + ((long long)key * (D / 2) + (c % CPRo) * (EPC / 2)) * 2);
+#pragma unroll
+            for (int e = 0; e < EPC / 4; ++e) tab[u][e] = src[e];
+        }
+    }
+    __syncthreads();
+    T* __restrict__ dkp = static_cast<T*>(a.dk);
+    T* __restrict__ dvp = static_cast<T*>(a.dv);
+#pragma unroll
+    for (int u = 0; u < (2 * NCK + NT - 1) / NT; ++u) {
+        const int c = tid + u * NT;
+        if (c >= 2 * NCK) break;
+        const int tsel = c / NCK;
+        const int cc = c % NCK;
+        const int kl = cc / CPRo, pt = cc % CPRo;
+        const int key = j * BN + kl;
+        if (key >= a.T) continue;
+        const float* src0 = part + (size_t)(kl >> 5) * 2 * 32 * PS + (size_t)tsel * 32 * PS + (size_t)(kl & 31) * PS + pt * EPC;
+        constexpr size_t QSTEP = (size_t)NKH * 2 * 32 * PS;  // floats between query blocks
+        float x[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+            f32x4 s4 = *reinterpret_cast<const f32x4*>(src0 + (NQH - 1) * QSTEP + e);
+#pragma unroll
+            for (int o = NQH - 2; o >= 0; --o) {
+                const f32x4 p4 = *reinterpret_cast<const f32x4*>(src0 + o * QSTEP + e);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s4[v] = p4[v] + s4[v];
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[e + v] = tsel == 0 ? s4[v] * a.scale : s4[v];
+        }
+        if (tsel == 0 && a.rope_cs != nullptr) {
+            // dK_raw = R(-phi) dK on each pair (2p, 2p + 1) of the segment.
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4) {
+                const f32x4 wv = tab[u < NDK ? u : 0][e / 4];
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const float x0 = x[e + 2 * v], x1 = x[e + 2 * v + 1];
+                    rope_rotate(x0, x1, wv[2 * v], -wv[2 * v + 1], &x[e + 2 * v], &x[e + 2 * v + 1]);
+                }
+            }
+        }
+        Vec16<T> out;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) out.set(e, from_f32<T>(x[e]));
+        T* dst = (tsel == 0 ? dkp : dvp) + (((long long)b * a.T + key) * a.Hkv + kvh) * D + pt * EPC;
+        st16(dst, out);
+    }
+}
+
+// The same end of a dK/dV item for head_dim 128, whose kernels have no registers to spare: the
+// partials are summed in NQH - 1 rounds through a region of one query block's size, in the
+// same order, and the totals leave through LDS as 16-byte row segments.
+template <typename T, int D, int NKH, int NQH, int BN, int NT>
+__device__ __forceinline__ void dkdv_epilogue_rounds(const BwdArgs& a, char* smem, f32x16 (&dkacc)[D / 32],
                                               f32x16 (&dvacc)[D / 32], int j, int kvh, int b) {
     constexpr int NDB = D / 32;
     constexpr int EPC = 16 / sizeof(T);
@@ -248,6 +353,15 @@ __device__ __forceinline__ void dkdv_epilogue(const BwdArgs& a, char* smem, f32x
         T* dst = (tsel == 0 ? dkp : dvp) + (((long long)b * a.T + key) * a.Hkv + kvh) * D + part * EPC;
         st16(dst, out);
     }
+}
+
+template <typename T, int D, int NKH, int NQH, int BN, int NT>
+__device__ __forceinline__ void dkdv_epilogue(const BwdArgs& a, char* smem, f32x16 (&dkacc)[D / 32],
+                                              f32x16 (&dvacc)[D / 32], int j, int kvh, int b) {
+    if constexpr (D <= 64)
+        dkdv_epilogue_all<T, D, NKH, NQH, BN, NT>(a, smem, dkacc, dvacc, j, kvh, b);
+    else
+        dkdv_epilogue_rounds<T, D, NKH, NQH, BN, NT>(a, smem, dkacc, dvacc, j, kvh, b);
 }
 
 // One workgroup of the dK/dV role: key tile j of K/V head kvh in batch b.  Each wave takes
@@ -567,11 +681,10 @@ struct DkdvDmaCfg {
     static constexpr size_t BYTES = NST * STAGE;
     static constexpr int NPIECE = BM / 8;          // 1 KB copies per tile
     static constexpr int PPW = NPIECE / NW;        // copies per wave per tile
-    static constexpr size_t RED_BYTES = (size_t)NKH * 2 * NDB * 16 * 64 * sizeof(float);
+    static constexpr size_t LDS = BYTES > dkdv_epi_bytes<D, NKH, NQH>() ? BYTES : dkdv_epi_bytes<D, NKH, NQH>();
     static_assert(NPIECE % NW == 0, "every wave issues the same number of copies");
     static_assert(STAGE % 16 == 0, "stage alignment");
-    static_assert(RED_BYTES <= BYTES, "reduction buffer must fit in the staging region");
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier: this wave's vector-memory operations but the
@@ -857,6 +970,13 @@ struct DqCfg {
     static constexpr int NCH = (SK * CPR + NT - 1) / NT;  // chunks per thread per tensor
     static constexpr int KBUF = SK * KS;
     static constexpr int STAGE = 2 * KBUF;  // K, V row-major
+    // Up to head_dim 64 the (cos, sin) rows of the workgroup's query rows (inverse RoPE of dQ)
+    // are staged once in LDS behind the two stages; TAB_ROWS is the most query rows a
+    // workgroup takes (32 per wave of a head, at most four waves per head).
+    static constexpr bool TAB = D <= 64;
+    static constexpr int TAB_ROWS = 128;
+    static constexpr size_t TAB_OFF = 2 * (size_t)STAGE * sizeof(T);
+    static constexpr size_t BYTES = TAB_OFF + (TAB ? (size_t)TAB_ROWS * D * sizeof(float) : 0);
 };
 
 // One workgroup of the dQ role: item it (0 = the longest query tile) of K/V head kvh in
@@ -1027,10 +1147,31 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
         }
     };
 
+    // The (cos, sin) rows of this workgroup's query rows, [BM][D] floats, staged in LDS by
+    // 16-byte pieces while tile 0 is in flight (used only after the loop).
+    constexpr int TPT = C::TAB ? (C::TAB_ROWS * D / 4 + C::NT - 1) / C::NT : 0;  // pieces per thread
+    [[maybe_unused]] f32x4 tabv[TPT > 0 ? TPT : 1];
+    const bool stage_tab = C::TAB && a.rope_cs != nullptr && BM <= C::TAB_ROWS;
+    if (stage_tab) {
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+            const int c = tid + u * C::NT;  // piece: row c / (D / 4), floats 4 (c % (D / 4)) ..
+            const int t = min(tile * BM + min(c / (D / 4), BM - 1), a.T - 1);
+            tabv[u] = *reinterpret_cast<const f32x4*>(a.rope_cs + (long long)t * D + 4 * (c % (D / 4)));
+        }
+    }
     // Tile s sits in register set s % NSET until it is committed at the start of iteration
     // s - 1; the set is then refilled with tile s + NSET.
     fetch(sa, 0);
     commit(sa, 0);
+    if (stage_tab) {
+        float* tabs = reinterpret_cast<float*>(smem_raw + C::TAB_OFF);
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+            const int c = tid + u * C::NT;
+            if (c < BM * D / 4) *reinterpret_cast<f32x4*>(tabs + 4 * c) = tabv[u];
+        }
+    }
     // The LSE / D loads were issued before tile 0's, which the commit has waited for.
     settle(lse2);
     settle(dtv);
@@ -1073,7 +1214,8 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, char* smem_raw, int it
     if (a.rope_cs != nullptr) {
         // dQ_raw = R(-phi) dQ.  Pair (d, d+1) sits in registers (r, r+1), r even, of this lane;
         // one 16-byte table read gives (cos, sin) of two consecutive pairs.
-        const float4* cs = reinterpret_cast<const float4*>(a.rope_cs + (long long)tq * D);
+        const float4* cs = stage_tab ? reinterpret_cast<const float4*>(smem_raw + C::TAB_OFF) + (tq - tile * BM) * (D / 4)
+                                     : reinterpret_cast<const float4*>(a.rope_cs + (long long)tq * D);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -1145,8 +1287,8 @@ struct BwdKernelCfg {
     static constexpr int BNQ = (D == 128) ? 32 : 64;  // dQ role key tile
     using Dk = DkdvCfg<T, D, 16 * NW>;
     using Dq = DqCfg<T, D, BNQ, NW>;
-    static constexpr size_t DQ_BYTES = 2 * (size_t)Dq::STAGE * sizeof(T);
-    static constexpr size_t DK_BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<BM, kDmaQbShared, 64, kDmaStagesShared>::BYTES : Dk::BYTES;
+    static constexpr size_t DQ_BYTES = Dq::BYTES;
+    static constexpr size_t DK_BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<BM, kDmaQbShared, 64, kDmaStagesShared>::LDS : Dk::LDS;
     static constexpr size_t BYTES = DK_BYTES > DQ_BYTES ? DK_BYTES : DQ_BYTES;
     static_assert(Dk::NW == NW, "dK/dV role must use every wave");
     static_assert(!kDkdvDma<T, D> || DkdvDmaCfg<BM, kDmaQbShared, 64, kDmaStagesShared>::NW == NW, "waves");
@@ -1207,7 +1349,7 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 && D >= 128) ? 2 : 1) void
     constexpr int BNQ = (D == 128 || NW == 12) ? 32 : 64;
     constexpr int SUB = (sizeof(T) == 2 && NW == 12) ? 4 : 1;
     using Dq = DqCfg<T, D, BNQ, NW, SUB>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * (size_t)Dq::STAGE * sizeof(T)];
+    __shared__ __attribute__((aligned(16))) char smem[Dq::BYTES];
     const int HB = a.B * a.Hkv;
     const int m = blockIdx.x / HB;
     const int rem = blockIdx.x % HB;
@@ -1224,7 +1366,7 @@ struct DkdvSolo {
     static constexpr int BN = D <= 64 ? 128 : 64;
     using Cfg = DkdvCfg<T, D, 128, 2, BN>;
     static constexpr int NT = 64 * Cfg::NW;
-    static constexpr size_t BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<128, 2, BN, kDmaStagesSolo>::BYTES : Cfg::BYTES;
+    static constexpr size_t BYTES = kDkdvDma<T, D> ? DkdvDmaCfg<128, 2, BN, kDmaStagesSolo>::LDS : Cfg::LDS;
 };
 template <typename T, int D>
 __global__ __launch_bounds__((DkdvSolo<T, D>::NT), 1) void bwd_dkdv_kernel(BwdArgs a) {
