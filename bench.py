@@ -349,8 +349,10 @@ def time_projections(name, steps, warmup, torch, ea, W):
     """The projections around one attention layer of a workload (model dimension C = Hq D):
     qkv_proj with RoPE (x [B*T, C] by w_qkv [C, (Hq + 2 Hkv) D]), the output projection
     y = o W_o, its backward (do = dy W_o^T, dW_o = o^T dy) and qkv_proj_bwd (dx and dW_qkv).
-    Average microseconds per call from HIP events on the launch stream, and TFLOP/s at
-    2 M N K per product against the dense MFMA peak of the dtype."""
+    The two weight gradients are timed plain and with split K (gemm_ws, qkv_proj_bwd_ws); the
+    totals count the split ones, which a layer would call.  Average microseconds per call from
+    HIP events on the launch stream, and TFLOP/s at 2 M N K per product against the dense
+    MFMA peak of the dtype."""
     w = W.WORKLOADS[name]
     log("[bench] projections of workload %s" % name)
     inp = W.make_proj_inputs(w)
@@ -371,6 +373,10 @@ def time_projections(name, steps, warmup, torch, ea, W):
     dtc = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
     stream = torch.cuda.current_stream(dev).cuda_stream
     p = lambda t: t.data_ptr()  # noqa: E731
+    # Split-K workspaces of the two weight gradients (few output tiles, K = B T).
+    ws_o = L.gemm_workspace_size(Hq * D, C, M, 1, 0, dtc)
+    ws_q = L.qkv_proj_bwd_workspace_size(B, T, C, Hq, Hkv, D, dtc)
+    ws = torch.empty(max(ws_o, ws_q, 256), device=dev, dtype=torch.uint8)
     calls = [
         ("qkv_proj_rope", 2 * M * Nq * C, L.qkv_proj,
          (p(x), p(wq), p(q), p(k), p(v), B, T, C, Hq, Hkv, D, dtc, 1, w.base, 0, stream)),
@@ -380,8 +386,12 @@ def time_projections(name, steps, warmup, torch, ea, W):
          (p(dy), p(wo), p(do), M, Hq * D, C, C, C, Hq * D, 0, 1, dtc, stream)),
         ("out_proj_bwd_dw", 2 * M * C * Hq * D, L.gemm,
          (p(o), p(dy), p(dwo), Hq * D, C, M, Hq * D, C, C, 1, 0, dtc, stream)),
+        ("out_proj_bwd_dw_splitk", 2 * M * C * Hq * D, L.gemm_ws,
+         (p(o), p(dy), p(dwo), Hq * D, C, M, Hq * D, C, C, 1, 0, dtc, p(ws), ws.numel(), stream)),
         ("qkv_proj_bwd", 2 * 2 * M * Nq * C, L.qkv_proj_bwd,
          (p(x), p(wq), p(q), p(k), p(v), p(dx), p(dwq), B, T, C, Hq, Hkv, D, dtc, stream)),
+        ("qkv_proj_bwd_splitk", 2 * 2 * M * Nq * C, L.qkv_proj_bwd_ws,
+         (p(x), p(wq), p(q), p(k), p(v), p(dx), p(dwq), B, T, C, Hq, Hkv, D, dtc, p(ws), ws.numel(), stream)),
     ]
     out = {"config": dict(w.describe(), model_dim=C), "calls": steps, "kernels": {}}
     total_us, total_flops = 0.0, 0
@@ -399,8 +409,9 @@ def time_projections(name, steps, warmup, torch, ea, W):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1000.0 / steps
         tf = flops / (us * 1e-6) / 1e12
-        total_us += us
-        total_flops += flops
+        if cname not in ("out_proj_bwd_dw", "qkv_proj_bwd"):  # superseded by the split-K calls
+            total_us += us
+            total_flops += flops
         out["kernels"][cname] = {"us_per_call": round(us, 2), "flops": flops, "tflops": round(tf, 2),
                                  "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4)}
     out["total_us"] = round(total_us, 2)

@@ -14,9 +14,9 @@ built, or the tensors are not on a ROCm device, the calls raise.
     attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv)        -> attn_bwd, no allocation
     attn_decode(q, k_cache, v_cache, scale=None, ...)         -> (o, lse) for the last Tq rows
     attn_fwd_noncausal / attn_bwd_noncausal                   -> as attn_fwd / attn_bwd, no mask
-    gemm(a, b, trans_a=False, trans_b=False, out=None)        -> op(a) @ op(b)
+    gemm(a, b, trans_a=False, trans_b=False, out=None, split_k=False) -> op(a) @ op(b)
     qkv_proj(x, w_qkv, Hq, Hkv, D, rope=True, base=1e4, ...)  -> (q, k, v) [B, T, H, D]
-    qkv_proj_bwd(x, w_qkv, dq, dk, dv)                         -> (dx, dw_qkv)
+    qkv_proj_bwd(x, w_qkv, dq, dk, dv, split_k=False)          -> (dx, dw_qkv)
 
 Layouts: q, o, dout, dq [B, T, Hq, D]; k, v, dk, dv [B, T, Hkv, D]; lse [B, Hq, T] fp32.
 dtype float32 or bfloat16.  head_dim 32, 64 or 128 for attention.
@@ -33,7 +33,7 @@ __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "att
            "attn_fwd_rope_workspace_size", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
            "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "gemm",
-           "qkv_proj", "qkv_proj_bwd", "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH", "EA_F32",
+           "qkv_proj", "qkv_proj_bwd", "gemm_workspace_size", "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH", "EA_F32",
            "EA_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeuler_attn.so")
@@ -99,10 +99,18 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.restype = ci
     L.gemm.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, vp]
     L.gemm.restype = ci
+    L.gemm_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.gemm_workspace_size.restype = sz
+    L.gemm_ws.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.gemm_ws.restype = ci
     L.qkv_proj.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, cd, ci, vp]
     L.qkv_proj.restype = ci
     L.qkv_proj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
     L.qkv_proj_bwd.restype = ci
+    L.qkv_proj_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    L.qkv_proj_bwd_workspace_size.restype = sz
+    L.qkv_proj_bwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.qkv_proj_bwd_ws.restype = ci
     L.euler_attn_status_string.argtypes = [ci]
     L.euler_attn_status_string.restype = ctypes.c_char_p
     L.euler_attn_version.argtypes = []
@@ -471,9 +479,19 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float 
     return o, l
 
 
+def gemm_workspace_size(M: int, N: int, K: int, trans_a: bool = False, trans_b: bool = False,
+                        dtype=torch.bfloat16) -> int:
+    """Bytes of the workspace that lets gemm(..., split_k=True) split K for this shape (0: none)."""
+    code = EA_F32 if dtype == torch.float32 else EA_BF16
+    return int(lib().gemm_workspace_size(M, N, K, int(bool(trans_a)), int(bool(trans_b)), code))
+
+
 def gemm(a: torch.Tensor, b: torch.Tensor, trans_a: bool = False, trans_b: bool = False,
-         out: torch.Tensor | None = None) -> torch.Tensor:
-    """op(a) @ op(b) for contiguous 2-D tensors (op transposes when its flag is set)."""
+         out: torch.Tensor | None = None, split_k: bool = False,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """op(a) @ op(b) for contiguous 2-D tensors (op transposes when its flag is set).  With
+    split_k (gemm_ws), a product with few output tiles and a long K splits K over more
+    workgroups, through a workspace (allocated here when not given)."""
     _check("a", a, 2)
     _check("b", b, 2, a.device, a.dtype)
     M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
@@ -484,9 +502,20 @@ def gemm(a: torch.Tensor, b: torch.Tensor, trans_a: bool = False, trans_b: bool 
     _check("out", c, 2, a.device, a.dtype)
     if tuple(c.shape) != (M, N):
         raise ValueError("out must be [%d, %d]" % (M, N))
+    ta, tb = int(bool(trans_a)), int(bool(trans_b))
+    if split_k or workspace is not None:
+        if workspace is None:
+            need = int(lib().gemm_workspace_size(M, N, K, ta, tb, _dtype_code(a)))
+            workspace = torch.empty(max(need, 256), device=a.device, dtype=torch.uint8)
+        wp, wb = _ws_args(workspace, a.device)
+        with torch.cuda.device(a.device):
+            st = lib().gemm_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, a.shape[1], b.shape[1], N,
+                               ta, tb, _dtype_code(a), wp, wb, _stream(a.device))
+        _raise(st, "gemm_ws")
+        return c
     with torch.cuda.device(a.device):
         st = lib().gemm(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, a.shape[1], b.shape[1], N,
-                        int(bool(trans_a)), int(bool(trans_b)), _dtype_code(a), _stream(a.device))
+                        ta, tb, _dtype_code(a), _stream(a.device))
     _raise(st, "gemm")
     return c
 
@@ -515,9 +544,11 @@ def qkv_proj(x: torch.Tensor, w_qkv: torch.Tensor, Hq: int, Hkv: int, D: int, ro
 
 
 def qkv_proj_bwd(x: torch.Tensor, w_qkv: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
-                 dv: torch.Tensor, dx: torch.Tensor | None = None, dw_qkv: torch.Tensor | None = None):
+                 dv: torch.Tensor, dx: torch.Tensor | None = None, dw_qkv: torch.Tensor | None = None,
+                 split_k: bool = False, workspace: torch.Tensor | None = None):
     """dx = [dq | dk | dv] w_qkv^T and dw_qkv = x^T [dq | dk | dv] (dq, dk: gradients of the
-    projections before RoPE).  Returns (dx, dw_qkv)."""
+    projections before RoPE).  With split_k (qkv_proj_bwd_ws) the products may split K, as
+    gemm(..., split_k=True).  Returns (dx, dw_qkv)."""
     _check("x", x, 3)
     _check("w_qkv", w_qkv, 2, x.device, x.dtype)
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
@@ -531,6 +562,17 @@ def qkv_proj_bwd(x: torch.Tensor, w_qkv: torch.Tensor, dq: torch.Tensor, dk: tor
     _check("dw_qkv", dw, 2, x.device, x.dtype)
     if dx.shape != x.shape or dw.shape != w_qkv.shape:
         raise ValueError("dx / dw_qkv must match x / w_qkv")
+    if split_k or workspace is not None:
+        if workspace is None:
+            need = int(lib().qkv_proj_bwd_workspace_size(B, T, C, Hq, Hkv, D, _dtype_code(x)))
+            workspace = torch.empty(max(need, 256), device=x.device, dtype=torch.uint8)
+        wp, wb = _ws_args(workspace, x.device)
+        with torch.cuda.device(x.device):
+            st = lib().qkv_proj_bwd_ws(x.data_ptr(), w_qkv.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), dx.data_ptr(), dw.data_ptr(), B, T, C, Hq, Hkv, D,
+                                       _dtype_code(x), wp, wb, _stream(x.device))
+        _raise(st, "qkv_proj_bwd_ws")
+        return dx, dw
     with torch.cuda.device(x.device):
         st = lib().qkv_proj_bwd(x.data_ptr(), w_qkv.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                 dx.data_ptr(), dw.data_ptr(), B, T, C, Hq, Hkv, D, _dtype_code(x),

@@ -3,9 +3,11 @@
 // Every entry point validates all of its arguments before anything is enqueued (no HIP
 // call happens on an invalid call), then hands off to the internal launchers.  Nothing is
 // allocated, freed or synchronised here.  Declarations and the contract: euler_attn.h.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 
 #include "ea_kernels.h"
@@ -501,13 +503,21 @@ ea_status check_qkv_sizes(int B, int T, int C, int Hq, int Hkv, int D, ea_dtype 
     return EA_OK;
 }
 
-}  // namespace
+// The split-K workspace of one product: 256-byte aligned, at least `need` bytes (may be NULL
+// when need is 0), overlapping none of the operands.
+ea_status check_splitk_ws(const void* ws, size_t bytes, size_t need, std::initializer_list<Range> others) {
+    if (need == 0) return EA_OK;
+    if (!ws) return EA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EA_ERR_ALIGN;
+    if (bytes < need) return EA_ERR_WORKSPACE;
+    const Range rw = range(ws, need);
+    for (Range r : others)
+        if (overlap(rw, r)) return EA_ERR_ALIAS;
+    return EA_OK;
+}
 
-extern "C" {
-
-ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
-               int ldc, int trans_a, int trans_b, ea_dtype dt, hipStream_t stream) {
-    if (!a || !b || !c) return EA_ERR_NULL;
+// Shape checks of gemm; 0 when the product is supported.
+ea_status check_gemm(int M, int N, int K, int lda, int ldb, int ldc, int trans_a, int trans_b, ea_dtype dt) {
     if (M < 1 || N < 1 || K < 1) return EA_ERR_INVALID_ARG;
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return EA_ERR_INVALID_ARG;
     if (!dtype_ok(dt) || (trans_a == 1 && trans_b == 1)) return EA_ERR_UNSUPPORTED;
@@ -515,19 +525,52 @@ ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int l
     // 16-byte chunks along every contiguous dimension that is loaded or stored.
     if (N % epc != 0 || ((trans_a == 0 || trans_b == 1) && K % epc != 0) || (trans_a == 1 && M % epc != 0))
         return EA_ERR_UNSUPPORTED;
+    const long long a_cols = trans_a ? M : K, b_cols = trans_b ? K : N;
+    if (lda < a_cols || ldb < b_cols || ldc < N) return EA_ERR_INVALID_ARG;
+    if (lda % epc || ldb % epc || ldc % epc) return EA_ERR_ALIGN;
+    return EA_OK;
+}
+
+ea_status gemm_impl(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+                    int ldc, int trans_a, int trans_b, ea_dtype dt, void* ws, size_t ws_bytes,
+                    bool use_ws, hipStream_t stream) {
+    if (!a || !b || !c) return EA_ERR_NULL;
+    ea_status st = check_gemm(M, N, K, lda, ldb, ldc, trans_a, trans_b, dt);
+    if (st != EA_OK) return st;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return EA_ERR_ALIGN;
     const long long a_rows = trans_a ? K : M, a_cols = trans_a ? M : K;
     const long long b_rows = trans_b ? N : K, b_cols = trans_b ? K : N;
-    if (lda < a_cols || ldb < b_cols || ldc < N) return EA_ERR_INVALID_ARG;
-    if (lda % epc || ldb % epc || ldc % epc || !aligned16(a) || !aligned16(b) || !aligned16(c))
-        return EA_ERR_ALIGN;
     const size_t es = elem_size(dt);
+    const Range ra = range(a, span_bytes(a_rows, a_cols, lda, es));
+    const Range rb = range(b, span_bytes(b_rows, b_cols, ldb, es));
     const Range rc = range(c, span_bytes(M, N, ldc, es));
-    if (overlap(rc, range(a, span_bytes(a_rows, a_cols, lda, es))) ||
-        overlap(rc, range(b, span_bytes(b_rows, b_cols, ldb, es))))
-        return EA_ERR_ALIAS;
+    if (overlap(rc, ra) || overlap(rc, rb)) return EA_ERR_ALIAS;
+    const size_t need = use_ws ? ea::gemm_splitk_bytes(M, N, K, static_cast<ea::IoType>(dt)) : 0;
+    if ((st = check_splitk_ws(ws, ws_bytes, need, {ra, rb, rc})) != EA_OK) return st;
     const ea::GemmSeg sa{a, lda, 0}, sb{b, ldb, 0}, sc{c, ldc, 0};
     return from_hip(ea::launch_gemm(&sa, 1, &sb, 1, &sc, 1, M, N, K, trans_a, trans_b,
-                                    static_cast<ea::IoType>(dt), nullptr, stream));
+                                    static_cast<ea::IoType>(dt), nullptr, stream, need ? ws : nullptr, need));
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+               int ldc, int trans_a, int trans_b, ea_dtype dt, hipStream_t stream) {
+    return gemm_impl(a, b, c, M, N, K, lda, ldb, ldc, trans_a, trans_b, dt, nullptr, 0, false, stream);
+}
+
+size_t gemm_workspace_size(int M, int N, int K, int trans_a, int trans_b, ea_dtype dt) {
+    if (check_gemm(M, N, K, trans_a ? M : K, trans_b ? K : N, N, trans_a, trans_b, dt) != EA_OK) return 0;
+    return ea::gemm_splitk_bytes(M, N, K, static_cast<ea::IoType>(dt));
+}
+
+ea_status gemm_ws(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+                  int ldc, int trans_a, int trans_b, ea_dtype dt, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    return gemm_impl(a, b, c, M, N, K, lda, ldb, ldc, trans_a, trans_b, dt, workspace, workspace_bytes,
+                     true, stream);
 }
 
 ea_status qkv_proj(const void* x, const void* w_qkv, void* q, void* k, void* v, int B, int T,
@@ -555,9 +598,14 @@ ea_status qkv_proj(const void* x, const void* w_qkv, void* q, void* k, void* v, 
                                     static_cast<ea::IoType>(dt), rope ? &r : nullptr, stream));
 }
 
-ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const void* dk,
-                       const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
-                       int Hkv, int D, ea_dtype dt, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ea_status qkv_proj_bwd_impl(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                            const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                            int Hkv, int D, ea_dtype dt, void* ws, size_t ws_bytes, bool use_ws,
+                            hipStream_t stream) {
     if (!x || !w_qkv || !dq || !dk || !dv || !dx || !dw_qkv) return EA_ERR_NULL;
     ea_status st = check_qkv_sizes(B, T, C, Hq, Hkv, D, dt);
     if (st != EA_OK) return st;
@@ -570,17 +618,51 @@ ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const v
                          range(dv, (size_t)(M * Hkv * D) * es)};
     const Range outs[] = {range(dx, (size_t)(M * C) * es), range(dw_qkv, (size_t)(C * N) * es)};
     if ((st = check_alias(ins, outs)) != EA_OK) return st;
+    const ea::IoType io = static_cast<ea::IoType>(dt);
+    // The two products run one after the other on the stream and share the workspace.
+    const size_t need_dx = use_ws ? ea::gemm_splitk_bytes((int)M, C, (int)N, io) : 0;
+    const size_t need_dw = use_ws ? ea::gemm_splitk_bytes(C, (int)N, (int)M, io) : 0;
+    if ((st = check_splitk_ws(ws, ws_bytes, std::max(need_dx, need_dw),
+                              {ins[0], ins[1], ins[2], ins[3], ins[4], outs[0], outs[1]})) != EA_OK)
+        return st;
     ea::GemmSeg g[3];
     qkv_segs(g, dq, dk, dv, Hq, Hkv, D);
     // dx = [dq | dk | dv] W^T: A split along K, B = W stored [C, N] = op(B)^T.
     const ea::GemmSeg wb{w_qkv, N, 0}, sdx{dx, C, 0};
-    hipError_t e = ea::launch_gemm(g, 3, &wb, 1, &sdx, 1, (int)M, C, (int)N, 0, 1,
-                                   static_cast<ea::IoType>(dt), nullptr, stream);
+    hipError_t e = ea::launch_gemm(g, 3, &wb, 1, &sdx, 1, (int)M, C, (int)N, 0, 1, io, nullptr, stream,
+                                   need_dx ? ws : nullptr, need_dx);
     if (e != hipSuccess) return from_hip(e);
     // dW = x^T [dq | dk | dv]: A = x stored [M, C] = op(A)^T, B split along N.
     const ea::GemmSeg xa{x, C, 0}, sdw{dw_qkv, N, 0};
-    return from_hip(ea::launch_gemm(&xa, 1, g, 3, &sdw, 1, C, (int)N, (int)M, 1, 0,
-                                    static_cast<ea::IoType>(dt), nullptr, stream));
+    return from_hip(ea::launch_gemm(&xa, 1, g, 3, &sdw, 1, C, (int)N, (int)M, 1, 0, io, nullptr, stream,
+                                    need_dw ? ws : nullptr, need_dw));
+}
+
+}  // namespace
+
+extern "C" {
+
+ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                       const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                       int Hkv, int D, ea_dtype dt, hipStream_t stream) {
+    return qkv_proj_bwd_impl(x, w_qkv, dq, dk, dv, dx, dw_qkv, B, T, C, Hq, Hkv, D, dt, nullptr, 0, false,
+                             stream);
+}
+
+size_t qkv_proj_bwd_workspace_size(int B, int T, int C, int Hq, int Hkv, int D, ea_dtype dt) {
+    if (check_qkv_sizes(B, T, C, Hq, Hkv, D, dt) != EA_OK) return 0;
+    const long long M = (long long)B * T, N = (long long)(Hq + 2 * Hkv) * D;
+    if (M > 0x7fffffffLL || N > 0x7fffffffLL) return 0;
+    const ea::IoType io = static_cast<ea::IoType>(dt);
+    return std::max(ea::gemm_splitk_bytes((int)M, C, (int)N, io), ea::gemm_splitk_bytes(C, (int)N, (int)M, io));
+}
+
+ea_status qkv_proj_bwd_ws(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                          const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                          int Hkv, int D, ea_dtype dt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return qkv_proj_bwd_impl(x, w_qkv, dq, dk, dv, dx, dw_qkv, B, T, C, Hq, Hkv, D, dt, workspace,
+                             workspace_bytes, true, stream);
 }
 
 }  // extern "C"

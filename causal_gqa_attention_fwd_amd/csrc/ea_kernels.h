@@ -91,8 +91,13 @@ struct GemmRope {
     int T, D, pos0;
     double base;
 };
+// splitk_ws (optional, splitk_bytes long): fp32 scratch that lets a product with few output tiles
+// and a long K split its K range over more workgroups (two launches); gemm_splitk_bytes gives the
+// size it uses (0: no split for this shape).
 hipError_t launch_gemm(const GemmSeg* a, int na, const GemmSeg* b, int nb, const GemmSeg* c,
                        int nc, int M, int N, int K, int trans_a, int trans_b, IoType dt,
-                       const GemmRope* rope, hipStream_t stream);
+                       const GemmRope* rope, hipStream_t stream, void* splitk_ws = nullptr,
+                       size_t splitk_bytes = 0);
+size_t gemm_splitk_bytes(int M, int N, int K, IoType dt);
 
 }  // namespace ea

@@ -51,6 +51,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
     int rope_mask;       // bit s: rotate the column pairs of C segment s (heads of rope_D)
     int rope_T, rope_D, rope_pos0;
+    int ksplit;          // split-K: slices of the K range (1: none)
+    float* part;         // split-K: fp32 partial tiles, [tile][slice][BM * BN] in register order
     RopeFreq f;
 };
 
@@ -124,7 +126,10 @@ struct GemmCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
+// MODE 0: C = op(A) op(B).  Split-K (a few output tiles, a long K): MODE 1 computes slice s of
+// the K range of a tile and stores its fp32 partial; MODE 2 then sums a tile's partials in slice
+// order (deterministic) and runs the epilogue.
+template <typename T, int TA, int TB, int BM, int BN, int WM, int WN, int MODE = 0>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     using C = GemmCfg<T, TA, TB, BM, BN, WM, WN>;
     using M_ = Mfma<T>;
@@ -143,14 +148,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     // XCD-aware tile order: workgroup L runs on XCD L % 8, and XCD x takes a contiguous run of
     // tiles (row-major over the tile grid), so the A rows and B columns its workgroups share
     // are fetched into its own L2 rather than into all eight.
+    // With split-K (MODE 1) the units are (tile, slice), the slices of a tile adjacent.
     const int ntiles = g.tiles_m * g.tiles_n;
+    const int nunits = MODE == 1 ? ntiles * g.ksplit : ntiles;
     const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
-    const int q8 = ntiles / kXcds, r8 = ntiles % kXcds;
-    const int tile = xcd < r8 ? xcd * (q8 + 1) + jx : r8 * (q8 + 1) + (xcd - r8) * q8 + jx;
+    const int q8 = nunits / kXcds, r8 = nunits % kXcds;
+    const int unit = xcd < r8 ? xcd * (q8 + 1) + jx : r8 * (q8 + 1) + (xcd - r8) * q8 + jx;
+    const int tile = MODE == 1 ? unit / g.ksplit : unit;
+    const int slice = MODE == 1 ? unit % g.ksplit : 0;
     const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
-    const int nk = (K + C::BK - 1) / C::BK;
+    const int nk_all = (K + C::BK - 1) / C::BK;
+    // K tiles [kt0, kt0 + nk) of this workgroup.
+    const int kt0 = MODE == 1 ? (int)((long long)slice * nk_all / g.ksplit) : 0;
+    const int nk = MODE == 1 ? (int)((long long)(slice + 1) * nk_all / g.ksplit) - kt0 : (MODE == 2 ? 0 : nk_all);
     const SegV<T> sa_(g.a), sb_(g.b);
 
     // Staging of one K tile (HBM -> registers), then registers -> LDS.  Every load is
@@ -274,9 +286,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     };
     auto fetch = [&](Stg& st, int kt) {
         if (a_split_k)
-            fetch_general(st, kt);
+            fetch_general(st, kt0 + kt);
         else
-            fetch_fast(st, kt);
+            fetch_fast(st, kt0 + kt);
     };
     // tail: this is the last K tile and K is not a multiple of BK (chunks past K -> zeros).
     auto commit = [&](Stg& st, int buf, bool tail) {
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
             }
         }
     };
-    const bool k_ragged = K % C::BK != 0;
+    const bool k_ragged = K % C::BK != 0 && kt0 + nk == nk_all;  // this range ends on a ragged tile
 
     f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -350,8 +362,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 
     // K tile s sits in register set s % NSET until it is committed at the start of step
     // s - 1; the set is then refilled with tile s + NSET.
-    fetch(sa, 0);
-    commit(sa, 0, k_ragged && nk == 1);
+    if (nk > 0) {
+        fetch(sa, 0);
+        commit(sa, 0, k_ragged && nk == 1);
+    }
     if constexpr (NSET == 2) {
         if (nk > 1) fetch(sb, 1);
         if (nk > 2) fetch(sa, 2);
@@ -373,6 +387,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         }
     } else {
         for (int kt = 0; kt < nk; ++kt) step(kt, sa);
+    }
+
+    // Split-K: partials in register order, [tile][slice][(mb, nb, r)][thread] (coalesced).
+    constexpr int PART = C::MB * C::NB * 16 * C::NT;  // floats per partial tile
+    if constexpr (MODE == 1) {
+        float* dst = g.part + ((size_t)tile * g.ksplit + slice) * PART + tid;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[((mb * C::NB + nb) * 16 + r) * C::NT] = acc[mb][nb][r];
+        return;
+    }
+    if constexpr (MODE == 2) {
+        const float* src = g.part + (size_t)tile * g.ksplit * PART + tid;
+        for (int sl = 0; sl < g.ksplit; ++sl) {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = src[(size_t)sl * PART + ((mb * C::NB + nb) * 16 + r) * C::NT];
+                        acc[mb][nb][r] = sl == 0 ? v : acc[mb][nb][r] + v;
+                    }
+        }
     }
 
     // Epilogue: lane = row m, registers 4*a4 .. 4*a4+3 of block nb = columns
@@ -422,31 +463,68 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     }
 }
 
+// Split-K slices for a grid of `tiles` output tiles and nk K tiles: enough (tile, slice) units
+// for two per CU, each slice keeping at least 8 K tiles; 1 (no split) when the tiles already
+// fill the chip or K is short.
+inline int pick_ksplit(long long tiles, int nk) {
+    if (tiles >= 256 || nk < 16) return 1;
+    const int want = (int)((512 + tiles - 1) / tiles);
+    return std::max(1, std::min(std::min(want, nk / 8), 8));
+}
+
 template <typename T, int TA, int TB, int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(GemmArgs g, hipStream_t stream) {
+hipError_t launch_cfg(GemmArgs g, float* ws, size_t ws_bytes, hipStream_t stream) {
     g.tiles_n = (g.N + BN - 1) / BN;
     g.tiles_m = (g.M + BM - 1) / BM;
     const long long blocks = (long long)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    using C = GemmCfg<T, TA, TB, BM, BN, WM, WN>;
+    // Only the 64 x 64 tiles split (the 128 x 128 ones are chosen when the tiles fill the chip).
+    if constexpr (BM == 64 && BN == 64) {
+        const int ks = ws ? pick_ksplit(blocks, (g.K + C::BK - 1) / C::BK) : 1;
+        const size_t need = (size_t)blocks * ks * BM * BN * sizeof(float);
+        if (ks > 1 && need <= ws_bytes && blocks * ks <= 0x7fffffffLL) {
+            g.ksplit = ks;
+            g.part = ws;
+            hipLaunchKernelGGL((gemm_kernel<T, TA, TB, BM, BN, WM, WN, 1>), dim3((unsigned)(blocks * ks)),
+                               dim3(64 * WM * WN), 0, stream, g);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((gemm_kernel<T, TA, TB, BM, BN, WM, WN, 2>), dim3((unsigned)blocks),
+                               dim3(64 * WM * WN), 0, stream, g);
+            return hipGetLastError();
+        }
+    }
+    g.ksplit = 1;
+    g.part = nullptr;
     hipLaunchKernelGGL((gemm_kernel<T, TA, TB, BM, BN, WM, WN>), dim3((unsigned)blocks),
                        dim3(64 * WM * WN), 0, stream, g);
     return hipGetLastError();
 }
 
+template <typename T, int BM, int BN, int WM, int WN>
+size_t ws_cfg(int M, int N, int K) {
+    constexpr int BK = GemmCfg<T, 0, 0, BM, BN, WM, WN>::BK;
+    const long long blocks = (long long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int ks = pick_ksplit(blocks, (K + BK - 1) / BK);
+    return ks > 1 ? (size_t)blocks * ks * BM * BN * sizeof(float) : 0;
+}
+
 // Tile shape: 128 x 128 (4 waves of 64 x 64) when that still gives every CU two tiles,
 // else 64 x 64 (4 waves of 32 x 32) for more, smaller workgroups.
+inline bool big_tiles(int M, int N) { return (long long)((M + 127) / 128) * ((N + 127) / 128) >= 512; }
+
 template <typename T, int TA, int TB>
-hipError_t launch_t(const GemmArgs& g, hipStream_t stream) {
-    const long long big = (long long)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (big >= 512) return launch_cfg<T, TA, TB, 128, 128, 2, 2>(g, stream);
-    return launch_cfg<T, TA, TB, 64, 64, 2, 2>(g, stream);
+hipError_t launch_t(const GemmArgs& g, float* ws, size_t ws_bytes, hipStream_t stream) {
+    if (big_tiles(g.M, g.N)) return launch_cfg<T, TA, TB, 128, 128, 2, 2>(g, ws, ws_bytes, stream);
+    return launch_cfg<T, TA, TB, 64, 64, 2, 2>(g, ws, ws_bytes, stream);
 }
 
 template <typename T>
-hipError_t launch_dt(const GemmArgs& g, int ta, int tb, hipStream_t stream) {
-    if (ta == 0 && tb == 0) return launch_t<T, 0, 0>(g, stream);
-    if (ta == 0 && tb == 1) return launch_t<T, 0, 1>(g, stream);
-    if (ta == 1 && tb == 0) return launch_t<T, 1, 0>(g, stream);
+hipError_t launch_dt(const GemmArgs& g, int ta, int tb, float* ws, size_t ws_bytes, hipStream_t stream) {
+    if (ta == 0 && tb == 0) return launch_t<T, 0, 0>(g, ws, ws_bytes, stream);
+    if (ta == 0 && tb == 1) return launch_t<T, 0, 1>(g, ws, ws_bytes, stream);
+    if (ta == 1 && tb == 0) return launch_t<T, 1, 0>(g, ws, ws_bytes, stream);
     return hipErrorInvalidValue;
 }
 
@@ -466,9 +544,14 @@ void fill_segs(Seg* dst, const GemmSeg* src, int n) {
 
 }  // namespace
 
+size_t gemm_splitk_bytes(int M, int N, int K, IoType dt) {
+    if (big_tiles(M, N)) return 0;
+    return dt == kF32 ? ws_cfg<float, 64, 64, 2, 2>(M, N, K) : ws_cfg<bf16, 64, 64, 2, 2>(M, N, K);
+}
+
 hipError_t launch_gemm(const GemmSeg* a, int na, const GemmSeg* b, int nb, const GemmSeg* c,
                        int nc, int M, int N, int K, int trans_a, int trans_b, IoType dt,
-                       const GemmRope* rope, hipStream_t stream) {
+                       const GemmRope* rope, hipStream_t stream, void* splitk_ws, size_t splitk_bytes) {
     GemmArgs g{};
     fill_segs(g.a, a, na);
     fill_segs(g.b, b, nb);
@@ -486,8 +569,9 @@ hipError_t launch_gemm(const GemmSeg* a, int na, const GemmSeg* b, int nb, const
         g.rope_pos0 = rope->pos0;
         fill_rope_freq(&g.f, rope->D, rope->base);
     }
-    return dt == kF32 ? launch_dt<float>(g, trans_a, trans_b, stream)
-                      : launch_dt<bf16>(g, trans_a, trans_b, stream);
+    float* ws = static_cast<float*>(splitk_ws);
+    return dt == kF32 ? launch_dt<float>(g, trans_a, trans_b, ws, splitk_bytes, stream)
+                      : launch_dt<bf16>(g, trans_a, trans_b, ws, splitk_bytes, stream);
 }
 
 }  // namespace ea

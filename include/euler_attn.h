@@ -288,6 +288,28 @@ ea_status gemm(const void* a, const void* b, void* c, int M, int N, int K, int l
                int ldc, int trans_a, int trans_b, ea_dtype dt, hipStream_t stream);
 
 /*
+ * gemm_ws -- gemm with a split of the K range.  A product with few output tiles and a long K
+ * (a weight gradient dW = x^T dy: [C, C'] output, K = B T rows) leaves most of the chip idle
+ * when each output tile is one workgroup; given a workspace, gemm_ws runs S slices of K per
+ * tile (S from the shape: enough workgroups for two per compute unit, at least eight K
+ * steps of the tile loop per slice, at most 8), each writing a float32 partial tile, and a
+ * second launch sums
+ * the S partials of every tile in slice order and rounds once to dt.  The result is
+ * deterministic (the same bits on every call) but may differ from gemm's in the last place,
+ * since the float32 sums are grouped differently.
+ * gemm_workspace_size(M, N, K, trans_a, trans_b, dt) -- bytes of workspace for this shape
+ * (0: no split for this shape, or an unsupported one; then gemm_ws is gemm and workspace may
+ * be NULL).  workspace: 256-byte aligned, at least that many bytes, contents on entry don't
+ * care, overwritten.  Errors: as gemm, plus workspace NULL (EA_ERR_NULL), misaligned
+ * (EA_ERR_ALIGN), too small (EA_ERR_WORKSPACE) or overlapping A, B or C (EA_ERR_ALIAS), each
+ * only when the size for the shape is not 0.
+ */
+size_t gemm_workspace_size(int M, int N, int K, int trans_a, int trans_b, ea_dtype dt);
+ea_status gemm_ws(const void* a, const void* b, void* c, int M, int N, int K, int lda, int ldb,
+                  int ldc, int trans_a, int trans_b, ea_dtype dt, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * qkv_proj -- the QKV projection of x [B, T, C] by w_qkv [C, (Hq + 2 Hkv) D] (row-major,
  * columns: the Hq query heads, then the Hkv key heads, then the Hkv value heads, D each):
  * q [B, T, Hq, D] = x Wq, k [B, T, Hkv, D] = x Wk, v [B, T, Hkv, D] = x Wv, in one launch.
@@ -312,6 +334,20 @@ ea_status qkv_proj(const void* x, const void* w_qkv, void* q, void* k, void* v, 
 ea_status qkv_proj_bwd(const void* x, const void* w_qkv, const void* dq, const void* dk,
                        const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
                        int Hkv, int D, ea_dtype dt, hipStream_t stream);
+
+/*
+ * qkv_proj_bwd_ws -- qkv_proj_bwd whose two products may split their K range as gemm_ws does
+ * (in practice dw_qkv, whose K = B T is long and whose output has few tiles).  The workspace
+ * (qkv_proj_bwd_workspace_size bytes, 256-byte aligned, may be NULL when that is 0) is shared
+ * by the two launches, which run in order on the stream.  Results deterministic, and as
+ * qkv_proj_bwd's up to float32 summation order; errors as qkv_proj_bwd plus gemm_ws's
+ * workspace errors.
+ */
+size_t qkv_proj_bwd_workspace_size(int B, int T, int C, int Hq, int Hkv, int D, ea_dtype dt);
+ea_status qkv_proj_bwd_ws(const void* x, const void* w_qkv, const void* dq, const void* dk,
+                          const void* dv, void* dx, void* dw_qkv, int B, int T, int C, int Hq,
+                          int Hkv, int D, ea_dtype dt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* euler_attn_status_string(ea_status s);

@@ -312,6 +312,63 @@ def test_gemm_validation(L):
     assert gemm_call(L, b=fake(2) + 64 * 64 * 2 - 16) == ALIAS
 
 
+def test_gemm_workspace_sizes(L):
+    # Split-K engages only for few output tiles (64 x 64) and a long K: slices from
+    # ceil(512 / tiles), at most K steps / 8 and 8; 4 bytes per element of each partial tile.
+    assert L.gemm_workspace_size(768, 768, 4096, 1, 0, BF16) == 144 * 4 * 64 * 64 * 4
+    assert L.gemm_workspace_size(768, 1280, 4096, 1, 0, BF16) == 240 * 3 * 64 * 64 * 4
+    assert L.gemm_workspace_size(64, 64, 8192, 0, 0, BF16) == 8 * 64 * 64 * 4
+    assert L.gemm_workspace_size(64, 64, 8192, 0, 0, F32) == 8 * 64 * 64 * 4
+    assert L.gemm_workspace_size(64, 64, 1024, 0, 0, BF16) == 2 * 64 * 64 * 4   # 16 K steps
+    assert L.gemm_workspace_size(64, 64, 960, 0, 0, BF16) == 0                  # 15 K steps
+    assert L.gemm_workspace_size(4096, 768, 1280, 0, 1, BF16) == 0              # 768 tiles
+    assert L.gemm_workspace_size(8192, 8192, 8192, 0, 0, BF16) == 0             # 128 x 128 tiles
+    assert L.gemm_workspace_size(64, 64, 8192, 1, 1, BF16) == 0                 # unsupported
+    assert L.gemm_workspace_size(64, 60, 8192, 0, 0, BF16) == 0
+    assert L.qkv_proj_bwd_workspace_size(4, 1024, 768, 12, 4, 64, BF16) == 240 * 3 * 64 * 64 * 4
+    assert L.qkv_proj_bwd_workspace_size(4, 1024, 768, 12, 5, 64, BF16) == 0    # Hq % Hkv
+
+
+def test_gemm_ws_validation(L):
+    need = 8 * 64 * 64 * 4
+
+    def call(ws=fake(3), nbytes=need, **kw):
+        a = dict(a=fake(0), b=fake(1), c=fake(2), M=64, N=64, K=8192, ta=0, tb=0, dt=BF16)
+        a.update(kw)
+        lda = a["M"] if a["ta"] else a["K"]
+        ldb = a["K"] if a["tb"] else a["N"]
+        return L.gemm_ws(a["a"], a["b"], a["c"], a["M"], a["N"], a["K"], lda, ldb, a["N"], a["ta"], a["tb"],
+                         a["dt"], ws, nbytes, None)
+    assert call(a=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(ws=fake(3) + 16) == ALIGN
+    assert call(nbytes=need - 1) == WS
+    assert call(ws=fake(0) + 4096) == ALIAS             # workspace inside A
+    assert call(ws=fake(2) - 256) == ALIAS              # workspace running into C
+    assert call(N=60) == UNSUP
+    assert call(M=0) == INVALID
+    # A shape that does not split needs no workspace: NULL is accepted up to the launch,
+    # so only the shape checks are exercised here.
+    assert call(ws=None, nbytes=0, K=512, N=60) == UNSUP
+
+
+def test_qkv_proj_bwd_ws_validation(L):
+    need = 240 * 3 * 64 * 64 * 4
+
+    def call(ws=fake(7), nbytes=need, **kw):
+        a = dict(x=fake(0), w=fake(1), dq=fake(2), dk=fake(3), dv=fake(4), dx=fake(5), dw=fake(6), B=4, T=1024,
+                 C=768, Hq=12, Hkv=4, D=64, dt=BF16)
+        a.update(kw)
+        return L.qkv_proj_bwd_ws(a["x"], a["w"], a["dq"], a["dk"], a["dv"], a["dx"], a["dw"], a["B"], a["T"],
+                                 a["C"], a["Hq"], a["Hkv"], a["D"], a["dt"], ws, nbytes, None)
+    assert call(dx=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(ws=fake(7) + 128) == ALIGN
+    assert call(nbytes=need - 256) == WS
+    assert call(ws=fake(6)) == ALIAS                    # workspace over dw
+    assert call(Hq=5) == INVALID
+
+
 def qkv(L, x=fake(0), w=fake(1), q=fake(2), k=fake(3), v=fake(4), B=2, T=16, C=64, Hq=4, Hkv=2, D=16,
         dt=BF16, rope=1, base=1e4, pos0=0):
     return L.qkv_proj(x, w, q, k, v, B, T, C, Hq, Hkv, D, dt, rope, base, pos0, None)

@@ -71,6 +71,55 @@ def test_gemm_leading_dimensions_and_repeat(dt):
     assert torch.equal(again, cbuf[:, :N])
 
 
+# Split-K shapes: few output tiles and a long K.  (768, 768, 4096) and (768, 1280, 4096) are the
+# weight gradients of the output and QKV projections at B T = 4096; the others reach the largest
+# split (8 slices of one tile), ragged M and N tiles, and a ragged last K tile (K % 64 != 0)
+# that falls in the last slice only.
+SPLIT_SHAPES = [(768, 768, 4096, 1, 0), (768, 1280, 4096, 1, 0), (64, 64, 8192, 0, 0),
+                (200, 136, 3000, 0, 1), (104, 72, 2056, 1, 0), (40, 24, 1064, 0, 0)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "M%d_N%d_K%d_ta%d_tb%d" % s)
+def test_gemm_split_k(dt, shape):
+    M, N, K, ta, tb = shape
+    code = ea.EA_F32 if dt == "f32" else ea.EA_BF16
+    need = ea.lib().gemm_workspace_size(M, N, K, ta, tb, code)
+    assert need > 0  # the split path is the one under test
+    seed = 4300 + M + N + K
+    say("[parity] gemm_ws %s M=%d N=%d K=%d ta=%d tb=%d seed %d, workspace %d B" % (dt, M, N, K, ta, tb, seed, need))
+    a = W.make_random((K, M) if ta else (M, K), seed, dt).cuda()
+    b = W.make_random((N, K) if tb else (K, N), seed + 1, dt).cuda()
+    ws = torch.full((need,), 0x7F, device="cuda", dtype=torch.uint8)  # stale contents don't matter
+    c = ea.gemm(a, b, trans_a=bool(ta), trans_b=bool(tb), workspace=ws)
+    c2 = ea.gemm(a, b, trans_a=bool(ta), trans_b=bool(tb), split_k=True)
+    torch.cuda.synchronize()
+    _check(dt, c, oracle.gemm(a, b, ta, tb), "gemm_ws")
+    assert torch.equal(c, c2)  # deterministic: the same bits from any workspace
+
+
+@pytest.mark.parametrize("name", ["gpu_model_bf16", "blog_t1024", "gpu_model_f32"])
+def test_qkv_proj_bwd_split_k(name):
+    w = W.WORKLOADS[name]
+    say("[parity] qkv_proj_bwd_ws workload %s" % name)
+    inp = W.make_proj_inputs(w)
+    x, wq = inp["x"].cuda(), inp["w_qkv"].cuda()
+    dq = W.make_random((w.B, w.T, w.Hq, w.D), w.seed + 611, w.dtype).cuda()
+    dk = W.make_random((w.B, w.T, w.Hkv, w.D), w.seed + 612, w.dtype).cuda()
+    dv = W.make_random((w.B, w.T, w.Hkv, w.D), w.seed + 613, w.dtype).cuda()
+    code = ea.EA_F32 if w.dtype == "f32" else ea.EA_BF16
+    assert ea.lib().qkv_proj_bwd_workspace_size(w.B, w.T, w.Hq * w.D, w.Hq, w.Hkv, w.D, code) > 0
+    dx, dw = ea.qkv_proj_bwd(x, wq, dq, dk, dv, split_k=True)
+    dx0, _ = ea.qkv_proj_bwd(x, wq, dq, dk, dv)
+    dx2, dw2 = ea.qkv_proj_bwd(x, wq, dq, dk, dv, split_k=True)
+    torch.cuda.synchronize()
+    rdx, rdw = oracle.qkv_proj_bwd(x, wq, dq, dk, dv)
+    _check(w.dtype, dx, rdx, "dx")
+    _check(w.dtype, dw, rdw, "dw_qkv (split K)")
+    assert torch.equal(dx, dx0)  # dx has enough tiles and is not split
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+
+
 @pytest.mark.parametrize("name,pos0", [("tiny_cpu_model", 0), ("gpu_model_f32", 5), ("gpu_model_bf16", 0),
                                        ("blog_t1024", 0)])
 def test_qkv_proj(name, pos0):
