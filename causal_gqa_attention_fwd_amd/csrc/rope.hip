@@ -41,11 +41,14 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeJob<T> job, int seq, int 
     constexpr int PPC = EPC / 2;         // pairs per chunk
     I u = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
     if (u >= (I)job.ntot) return;
+    // The tensor is chosen by selects between the two argument sets (loaded as scalars), not by
+    // indexing them with a per-lane value, which would load the pointers per lane and make
+    // every data load wait for that load first.
     const int which = u < (I)job.n0 ? 0 : 1;
     if (which) u -= (I)job.n0;
-    const T* x = job.x[which];
-    T* y = job.y[which];
-    const int H = job.H[which];
+    const T* x = which ? job.x[1] : job.x[0];
+    T* y = which ? job.y[1] : job.y[0];
+    const int H = which ? job.H[1] : job.H[0];
     const I cpr = (I)(D / EPC);  // chunks per row
     const I nhb = (I)((H + kHeadsPerThread - 1) / kHeadsPerThread);
     const int c = (int)(u % cpr);
@@ -106,11 +109,11 @@ __global__ __launch_bounds__(256) void rope_pair_kernel(RopeJob<T> job, int seq,
                                                         int inverse, RopeFreq f) {
     I u = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
     if (u >= (I)job.ntot) return;
-    const int which = u < (I)job.n0 ? 0 : 1;
+    const int which = u < (I)job.n0 ? 0 : 1;  // selects, as in rope_kernel
     if (which) u -= (I)job.n0;
-    const T* x = job.x[which];
-    T* y = job.y[which];
-    const int H = job.H[which];
+    const T* x = which ? job.x[1] : job.x[0];
+    T* y = which ? job.y[1] : job.y[0];
+    const int H = which ? job.H[1] : job.H[0];
     const I ppr = (I)(D / 2);  // pairs per row
     const I nhb = (I)((H + kHeadsPerThread - 1) / kHeadsPerThread);
     const int i = (int)(u % ppr);
