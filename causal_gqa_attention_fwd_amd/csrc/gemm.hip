@@ -170,14 +170,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     // while earlier ones are committed.  Rows past M or N load a real row: they only feed
     // outputs that are never stored.  Chunks past K load a real chunk too and are replaced
     // by zeros at commit (bit n of ok clear), as they would otherwise enter valid outputs.
-    constexpr int NSET = sizeof(T) == 2 ? 2 : 1;
+    // Register sets of staged K tiles in flight: two for bf16 (a third set for the 64 x 64 tiles
+    // measured slower), one for fp32.
+    constexpr int NSET = sizeof(T) != 2 ? 1 : 2;
     static_assert(C::NCA + C::NCB <= 32, "chunk mask");
     struct Stg {
         Vec16<T> a[C::NCA], b[C::NCB];
         uint32_t ok;
     };
-    Stg sa;
-    [[maybe_unused]] Stg sb;
+    Stg sets[NSET];
     // Per-chunk source addresses that do not change along K, computed once (the K loop only
     // adds its offset): A row / column bases (unless A is split along K, which takes the
     // general path below), B bases with their segment's leading dimension.
@@ -284,11 +285,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         }
         st.ok = ok;
     };
+    // Whole K tiles (all but a ragged last one) load through running per-chunk pointers that
+    // advance by one K tile per fetch (the fetches come in K order), which costs one 64-bit add
+    // per chunk instead of re-forming the address (a 64-bit product for the K-major operands)
+    // and the tail mask.
+    static_assert((C::A_ROWS * C::A_CPR) % C::NT == 0 && (C::B_ROWS * C::B_CPR) % C::NT == 0,
+                  "every staged chunk lies inside the tile (no unclamped spare chunks)");
+    const T* ap[C::NCA];
+    const T* bp[C::NCB];
+    long long bst[C::NCB];
+    const long long ast = TA == 0 ? (long long)C::BK : (long long)C::BK * sa_.ld0;
+#pragma unroll
+    for (int n = 0; n < C::NCA; ++n) {
+        if constexpr (TA == 0)
+            ap[n] = abase[n] + aoff[n] + (long long)kt0 * C::BK;
+        else
+            ap[n] = abase[n] + (long long)(kt0 * C::BK + aoff[n]) * sa_.ld0;
+    }
+#pragma unroll
+    for (int n = 0; n < C::NCB; ++n) {
+        if constexpr (TB == 0) {
+            bp[n] = bbase[n] + (long long)(kt0 * C::BK + boff[n]) * bld[n];
+            bst[n] = (long long)C::BK * bld[n];
+        } else {
+            bp[n] = bbase[n] + boff[n] + (long long)kt0 * C::BK;
+            bst[n] = C::BK;
+        }
+    }
+    auto fetch_run = [&](Stg& st) {
+#pragma unroll
+        for (int n = 0; n < C::NCA; ++n) {
+            st.a[n] = ld16(ap[n]);
+            ap[n] += ast;
+        }
+#pragma unroll
+        for (int n = 0; n < C::NCB; ++n) {
+            st.b[n] = ld16(bp[n]);
+            bp[n] += bst[n];
+        }
+    };
     auto fetch = [&](Stg& st, int kt) {
         if (a_split_k)
             fetch_general(st, kt0 + kt);
+        else if (K % C::BK != 0 && kt0 + kt == nk_all - 1)
+            fetch_fast(st, kt0 + kt);  // the ragged last tile: clamped addresses and the zero mask
         else
-            fetch_fast(st, kt0 + kt);
+            fetch_run(st);
     };
     // tail: this is the last K tile and K is not a multiple of BK (chunks past K -> zeros).
     auto commit = [&](Stg& st, int buf, bool tail) {
@@ -363,15 +405,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     // K tile s sits in register set s % NSET until it is committed at the start of step
     // s - 1; the set is then refilled with tile s + NSET.
     if (nk > 0) {
-        fetch(sa, 0);
-        commit(sa, 0, k_ragged && nk == 1);
+        fetch(sets[0], 0);
+        commit(sets[0], 0, k_ragged && nk == 1);
     }
-    if constexpr (NSET == 2) {
-        if (nk > 1) fetch(sb, 1);
-        if (nk > 2) fetch(sa, 2);
-    } else {
-        if (nk > 1) fetch(sa, 1);
-    }
+#pragma unroll
+    for (int j = 1; j <= NSET; ++j)
+        if (j < nk) fetch(sets[j % NSET], j);
     auto step = [&](int kt, Stg& nxt) {
         __syncthreads();  // tile kt visible in buffer kt&1; buffer (kt+1)&1 free
         if (kt + 1 < nk) {
@@ -380,13 +419,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         }
         compute(kt & 1);
     };
-    if constexpr (NSET == 2) {
-        for (int kt = 0; kt < nk; kt += 2) {
-            step(kt, sb);
-            if (kt + 1 < nk) step(kt + 1, sa);
-        }
-    } else {
-        for (int kt = 0; kt < nk; ++kt) step(kt, sa);
+    // Step kt commits tile kt + 1 from set (kt + 1) % NSET (the loop is unrolled NSET times so
+    // that the set is a constant).
+    for (int kt = 0; kt < nk; kt += NSET) {
+#pragma unroll
+        for (int j = 0; j < NSET; ++j)
+            if (kt + j < nk) step(kt + j, sets[(j + 1) % NSET]);
     }
 
     // Split-K: partials in register order, [tile][slice][(mb, nb, r)][thread] (coalesced).
