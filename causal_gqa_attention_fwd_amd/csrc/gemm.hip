@@ -548,13 +548,16 @@ size_t ws_cfg(int M, int N, int K) {
     return ks > 1 ? (size_t)blocks * ks * BM * BN * sizeof(float) : 0;
 }
 
-// Tile shape: 128 x 128 (4 waves of 64 x 64) when that still gives every CU two tiles,
-// else 64 x 64 (4 waves of 32 x 32) for more, smaller workgroups.
-inline bool big_tiles(int M, int N) { return (long long)((M + 127) / 128) * ((N + 127) / 128) >= 512; }
+// Tile shape: 128 x 128 (4 waves of 64 x 64) when that still gives every CU two tiles, or one
+// tile and a long K; else 64 x 64 (4 waves of 32 x 32) for more, smaller workgroups.
+inline bool big_tiles(int M, int N, int K) {
+    const long long t = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    return t >= 512 || (t >= 256 && K >= 2048);
+}
 
 template <typename T, int TA, int TB>
 hipError_t launch_t(const GemmArgs& g, float* ws, size_t ws_bytes, hipStream_t stream) {
-    if (big_tiles(g.M, g.N)) return launch_cfg<T, TA, TB, 128, 128, 2, 2>(g, ws, ws_bytes, stream);
+    if (big_tiles(g.M, g.N, g.K)) return launch_cfg<T, TA, TB, 128, 128, 2, 2>(g, ws, ws_bytes, stream);
     return launch_cfg<T, TA, TB, 64, 64, 2, 2>(g, ws, ws_bytes, stream);
 }
 
@@ -583,7 +586,7 @@ void fill_segs(Seg* dst, const GemmSeg* src, int n) {
 }  // namespace
 
 size_t gemm_splitk_bytes(int M, int N, int K, IoType dt) {
-    if (big_tiles(M, N)) return 0;
+    if (big_tiles(M, N, K)) return 0;
     return dt == kF32 ? ws_cfg<float, 64, 64, 2, 2>(M, N, K) : ws_cfg<bf16, 64, 64, 2, 2>(M, N, K);
 }
 

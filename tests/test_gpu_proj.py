@@ -30,8 +30,10 @@ def _check(dt, got, ref, what):
     assert e <= GEMM_TOL[dt], (what, e)
 
 
+# The last shape takes the 128 x 128 tiles (306 of them with a K of 2088) with ragged M, N and
+# K tails; the others the 64 x 64 tiles.
 SHAPES = [(1, 8, 8), (37, 40, 24), (130, 136, 72), (257, 264, 1000), (512, 768, 768),
-          (4096, 1280, 768)]
+          (4096, 1280, 768), (2056, 2184, 2088)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
