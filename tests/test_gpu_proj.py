@@ -122,6 +122,32 @@ def test_qkv_proj_bwd_split_k(name):
     assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
 
 
+# Short sequences where dx splits too (few rows, K = (Hq + 2 Hkv) D): its A operand is the three
+# gradient tensors side by side along K; with head_dim 32 and Hq + Hkv odd a K tile straddles
+# the dk / dv boundary inside the second slice.
+@pytest.mark.parametrize("case", [(1, 64, 12, 4, 64, "bf16"), (1, 50, 18, 9, 32, "bf16"), (2, 40, 16, 8, 64, "f32")],
+                         ids=lambda c: "B%d_T%d_H%d-%d_D%d_%s" % c)
+def test_qkv_proj_bwd_split_k_edges(case):
+    B, T, Hq, Hkv, D, dt = case
+    C, N = Hq * D, (Hq + 2 * Hkv) * D
+    code = ea.EA_F32 if dt == "f32" else ea.EA_BF16
+    assert ea.lib().gemm_workspace_size(B * T, C, N, 0, 1, code) > 0  # the dx product splits
+    seed = 4900 + T + Hq + D
+    say("[parity] qkv_proj_bwd_ws edge case %s seed %d" % (case, seed))
+    x = W.make_random((B, T, C), seed, dt).cuda()
+    wq = W.make_random((C, N), seed + 1, dt, scale=C ** -0.5).cuda()
+    dq = W.make_random((B, T, Hq, D), seed + 2, dt).cuda()
+    dk = W.make_random((B, T, Hkv, D), seed + 3, dt).cuda()
+    dv = W.make_random((B, T, Hkv, D), seed + 4, dt).cuda()
+    dx, dw = ea.qkv_proj_bwd(x, wq, dq, dk, dv, split_k=True)
+    dx2, dw2 = ea.qkv_proj_bwd(x, wq, dq, dk, dv, split_k=True)
+    torch.cuda.synchronize()
+    rdx, rdw = oracle.qkv_proj_bwd(x, wq, dq, dk, dv)
+    _check(dt, dx, rdx, "dx (split K)")
+    _check(dt, dw, rdw, "dw_qkv")
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+
+
 @pytest.mark.parametrize("name,pos0", [("tiny_cpu_model", 0), ("gpu_model_f32", 5), ("gpu_model_bf16", 0),
                                        ("blog_t1024", 0)])
 def test_qkv_proj(name, pos0):
