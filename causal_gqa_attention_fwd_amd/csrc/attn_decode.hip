@@ -250,8 +250,12 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
 }
 
 // The single launch for caches of at most NW chunks: one workgroup per (batch, K/V head, row
-// block), wave w computing chunk w; the partials then meet in LDS (over the V tiles, after a
-// barrier) and are merged exactly as decode_merge_kernel does, chunks in order.
+// block), wave w computing chunk w.  Each wave writes its partial (O_c, LSE_c) to its own LDS
+// region as soon as its chunk is done (the partials do not overlap the V tiles, so no wave
+// waits for another before writing).  The merge is decode_merge_kernel's, step for step:
+// one thread per (row, chunk) forms the weight e^{LSE_c - m}, and every thread then merges
+// the output elements it stores (the row's weights summed in chunk order, one reciprocal, the
+// chunks' values in order).
 // Waves of the single launch, sized so that each wave keeps the split launch's registers
 // (four waves per SIMD for bf16 head_dim 32, two for head_dim 64 and fp32 head_dim 32, one
 // for head_dim 128).
@@ -267,9 +271,11 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     constexpr int PST = D + 1;  // row stride of a partial (odd: lanes of one column on distinct banks)
     constexpr size_t V_BYTES = (size_t)NW * kKT * C::VS * sizeof(T);
     constexpr size_t P_BYTES = (size_t)NW * 32 * PST * sizeof(float);
-    __shared__ __attribute__((aligned(16))) char smem[(V_BYTES > P_BYTES ? V_BYTES : P_BYTES) + NW * 32 * sizeof(float)];
-    float* part = reinterpret_cast<float*>(smem);
-    float* wts = reinterpret_cast<float*>(smem + (V_BYTES > P_BYTES ? V_BYTES : P_BYTES));
+    static_assert(V_BYTES % 16 == 0 && V_BYTES + P_BYTES + 2 * NW * 32 * sizeof(float) <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) char smem[V_BYTES + P_BYTES + 2 * NW * 32 * sizeof(float)];
+    float* part = reinterpret_cast<float*>(smem + V_BYTES);
+    float* lses = reinterpret_cast<float*>(smem + V_BYTES + P_BYTES);  // LSE_c of (chunk, row)
+    float* wts = lses + NW * 32;                                        // its weight
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -284,43 +290,44 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     f32x16 oacc[C::NDB];
     float lse;
     decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, oacc, lse);
-    __syncthreads();  // every wave is done with its V tile
     {
         float* po = part + (size_t)w * 32 * PST + l32 * PST;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) po[db * 32 + acc_row(rr, half)] = oacc[db][rr];
-        if (half == 0) wts[w * 32 + l32] = lse;
+        if (half == 0) lses[w * 32 + l32] = lse;
     }
     __syncthreads();
-    // Row weights e^{LSE_c - m} / sum (m: the row's largest LSE_c; chunk 0 holds key 0, which
-    // every row sees, so m is finite), and the row's LSE.
+    // Chunk weights e^{LSE_c - m}, one thread per (row, chunk) (m: the row's largest LSE_c;
+    // chunk 0 holds key 0, which every row sees, so m is finite).
     const int nrows = min(32, a.R - rb * 32);
-    if (tid < nrows) {
+    const int wr = tid % 32, wch = tid / 32;
+    if (wr < nrows && wch < ns) {
         float m = -INFINITY;
-        for (int c = 0; c < ns; ++c) m = fmaxf(m, wts[c * 32 + tid]);
-        float z = 0.0f;
-        for (int c = 0; c < ns; ++c) {
-            const float ls = wts[c * 32 + tid];
-            const float wc = (ls == -INFINITY) ? 0.0f : expf(ls - m);
-            wts[c * 32 + tid] = wc;
-            z += wc;
-        }
-        const float iz = 1.0f / z;
-        for (int c = 0; c < ns; ++c) wts[c * 32 + tid] *= iz;
-        const int r = rb * 32 + tid;
-        const int ti = r / a.g, head = kvh * a.g + r % a.g;
-        a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
+        for (int c = 0; c < ns; ++c) m = fmaxf(m, lses[c * 32 + wr]);
+        const float ls = lses[wch * 32 + wr];
+        wts[wch * 32 + wr] = (ls == -INFINITY) ? 0.0f : expf(ls - m);
     }
     __syncthreads();
+    // Each thread merges the output elements it stores: the row's weights summed in chunk order,
+    // one reciprocal, then the chunks' values in order; the thread of column 0 writes the row's
+    // LSE = m + log(sum).
     for (int e = tid; e < nrows * D; e += ns * 64) {
         const int rl = e / D, d = e % D;
+        float z = 0.0f;
+        for (int c = 0; c < ns; ++c) z += wts[c * 32 + rl];
+        const float iz = 1.0f / z;
         float acc = 0.0f;
-        for (int c = 0; c < ns; ++c) acc += wts[c * 32 + rl] * part[((size_t)c * 32 + rl) * PST + d];
+        for (int c = 0; c < ns; ++c) acc += (wts[c * 32 + rl] * iz) * part[((size_t)c * 32 + rl) * PST + d];
         const int r = rb * 32 + rl;
         const int ti = r / a.g, head = kvh * a.g + r % a.g;
         static_cast<T*>(a.o)[(((long long)b * a.Tq + ti) * a.Hq + head) * D + d] = from_f32<T>(acc);
+        if (d == 0) {
+            float m = -INFINITY;
+            for (int c = 0; c < ns; ++c) m = fmaxf(m, lses[c * 32 + rl]);
+            a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = m + logf(z);
+        }
     }
 }
 
