@@ -100,6 +100,30 @@ def test_gemm_split_k(dt, shape):
     assert torch.equal(c, c2)  # deterministic: the same bits from any workspace
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gemm_split_k_leading_dimensions(dt):
+    # gemm_ws on operands and result inside wider buffers: the split path's partial and reduce
+    # launches read and write through the leading dimensions; the columns beyond N stay.
+    M, N, K, pad = 96, 80, 2048, 24
+    code = ea.EA_F32 if dt == "f32" else ea.EA_BF16
+    need = ea.lib().gemm_workspace_size(M, N, K, 1, 0, code)
+    assert need > 0
+    say("[parity] gemm_ws with leading dimensions, %s, workspace %d B" % (dt, need))
+    abuf = W.make_random((K, M + pad), 91, dt).cuda()
+    bbuf = W.make_random((K, N + pad), 92, dt).cuda()
+    cbuf = torch.full((M, N + pad), 3.0, device="cuda", dtype=abuf.dtype)
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    st = ea.lib().gemm_ws(abuf.data_ptr(), bbuf.data_ptr(), cbuf.data_ptr(), M, N, K, M + pad, N + pad,
+                          N + pad, 1, 0, code, ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    _check(dt, cbuf[:, :N], oracle.gemm(abuf[:, :M], bbuf[:, :N], 1, 0), "gemm_ws ld")
+    assert bool((cbuf[:, N:] == 3.0).all())
+    again = ea.gemm(abuf[:, :M].contiguous(), bbuf[:, :N].contiguous(), trans_a=True, split_k=True)
+    torch.cuda.synchronize()
+    assert torch.equal(again, cbuf[:, :N])
+
+
 @pytest.mark.parametrize("name", ["gpu_model_bf16", "blog_t1024", "gpu_model_f32"])
 def test_qkv_proj_bwd_split_k(name):
     w = W.WORKLOADS[name]
