@@ -339,6 +339,8 @@ constexpr int kMaxSplit = 256;
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     constexpr int CPL = D >= 64 ? D / 64 : 1;  // columns per lane
+    constexpr int NB = 16;                      // chunks whose values are loaded up front
+    constexpr int LPL = kMaxSplit / 64;         // LSE values per lane
     __shared__ float wsh[kMaxSplit];
     const int lane = threadIdx.x;
     const long long row = blockIdx.x;  // (b * Hkv + kvh) * R + r
@@ -348,28 +350,58 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     const int b = (int)(bk / a.Hkv);
     const int rb = r / 32, rl = r % 32;
     const long long item0 = (bk * a.nrb + rb) * a.nsplit;
+    const int ns = a.nsplit;
+    const bool cols = lane * CPL < D;
+    // Lanes past the row's columns (head_dim 32) read column 0 and store nothing.
+    const float* po = a.part_o + (item0 * 32 + rl) * D + (cols ? lane * CPL : 0);
+    // Every load that does not depend on another goes out first: the row's LSE_c values (lane
+    // sp % 64 holds chunk sp) and this lane's columns of the first NB chunks, so the kernel
+    // waits for memory once.
+    float lsv[LPL];
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) {
+        const int sp = lane + 64 * k;
+        const float v = a.part_lse[(item0 + min(sp, ns - 1)) * 32 + rl];  // clamped: no branch
+        lsv[k] = sp < ns ? v : -INFINITY;
+    }
+    float pv[NB][CPL];  // chunks past the last re-read the last one and are never used
+#pragma unroll
+    for (int sp = 0; sp < NB; ++sp)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) pv[sp][c] = po[(long long)min(sp, ns - 1) * 32 * D + c];
     float m = -INFINITY;
-    for (int sp = lane; sp < a.nsplit; sp += 64) m = fmaxf(m, a.part_lse[(item0 + sp) * 32 + rl]);
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) m = fmaxf(m, lsv[k]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float z = 0.0f;
-    for (int sp = lane; sp < a.nsplit; sp += 64) {
-        const float ls = a.part_lse[(item0 + sp) * 32 + rl];
-        const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
-        wsh[sp] = wgt;
-        z += wgt;
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) {
+        const int sp = lane + 64 * k;
+        if (sp < ns) {
+            const float wgt = (lsv[k] == -INFINITY) ? 0.0f : expf(lsv[k] - m);
+            wsh[sp] = wgt;
+            z += wgt;
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
     __syncthreads();
     const int ti = r / a.g, head = kvh * a.g + r % a.g;
-    if (lane * CPL < D) {
+    if (cols) {
         float acc[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
-        const float* po = a.part_o + (item0 * 32 + rl) * D + lane * CPL;
+#pragma unroll
+        for (int sp = 0; sp < NB; ++sp) {
+            if (sp < ns) {
+                const float wgt = wsh[sp];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] += wgt * pv[sp][c];
+            }
+        }
 #pragma unroll 8
-        for (int sp = 0; sp < a.nsplit; ++sp) {
+        for (int sp = NB; sp < ns; ++sp) {
             const float wgt = wsh[sp];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[c] += wgt * po[(long long)sp * 32 * D + c];
