@@ -11,9 +11,13 @@
 // there are few queries to reuse it), so the design is about bytes in flight, not matrix
 // cores:
 //  * Rows.  The g query heads sharing a K/V head and the Tq tokens form R = g * Tq rows,
-//    row r = i * g + hs; each wave takes a block of 32 rows as the 32 columns of its MFMA
+//    row r = i * g + hs; each wave takes a block of 32 rows as the columns of its MFMA
 //    tiles (S^T = K Q^T, O^T += V^T P^T, as in attn_fwd), so one read of a key row serves
-//    every head of the group and every new token.
+//    every head of the group and every new token.  bf16 at head_dim 64 and 128 uses 16 x 16
+//    x 32 products on 16-row halves of the block (a second half only where the block has
+//    more than 16 rows), since R is usually 16 or less: half the padding work, half the
+//    softmax lanes' values per tile, and far fewer registers when no block needs a second
+//    half.
 //  * Split over the cache (split-K): each wave streams its own chunk of keys, 32 at a time;
 //    K rows go straight from HBM into the operand registers (the "split" layout is 16-byte
 //    runs of a key row), V rows through a wave-private LDS tile for the transposing read of
@@ -204,9 +208,201 @@ __device__ __forceinline__ void decode_chunk(const DecArgs& a, T* Vs, int b, int
         for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= inv;
 }
 
+// bf16: the same chunk on 16 x 16 x 32 products, whose 16 columns hold the rows (the g heads x
+// Tq tokens of a group are 16 or fewer in the usual shapes, so the 32-column products of
+// decode_chunk compute mostly padding).  Rows rb * 32 + 16 hb + (lane % 16): hb = 0, and hb = 1
+// only when the block has more than 16 rows.  Lane groups q = lane / 16 hold, for each 16-key
+// block kb, the scores of keys 16 kb + 4 q + 0..3 (the accumulator rows 4 q .. 4 q + 3), so a
+// row's 32 keys of a tile sit in the four lanes with the same lane % 16.  For O^T += V^T P^T
+// the contraction slots 8 q + e take keys 4 q + e (e < 4) and 16 + 4 q + (e - 4): P^T comes
+// straight from the lane's own scores, V^T from two transposing reads of the LDS tile.  On
+// return oacc[hb][db][i] is O_c of row 16 hb + lane % 16, head_dim 16 db + 4 q + i (normalised
+// by its own row sums) and lse[hb] that row's LSE_c (natural log, -inf with no key).
+// Which launches take the 16-row products: bf16 with head_dim 64 and 128 (at head_dim 32 the
+// 32-row products measured faster).
+template <typename T, int D>
+constexpr bool kDec16 = sizeof(T) == 2 && D >= 64;
+
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x4 tr4(const bf16* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// NH: 16-row halves the kernel may meet (1 when every row block has at most 16 rows).
+template <int D, int NH>
+__device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b, int kvh, int rb, int sp,
+                                               f32x4 (&oacc)[NH][D / 16], float (&lse)[NH]) {
+    using T = bf16;
+    using C = DecCfg<T, D>;
+    constexpr int NST = D / 32;  // 32-deep steps over head_dim
+    constexpr int NDB = D / 16;  // 16-wide head_dim blocks of O
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int c16 = lane & 15;
+
+    const T* __restrict__ qp = static_cast<const T*>(a.q);
+    const T* __restrict__ kp = static_cast<const T*>(a.k);
+    const T* __restrict__ vp = static_cast<const T*>(a.v);
+    const int off = a.Tk - a.Tq;
+    const bool two = NH == 2 && rb * 32 + 16 < a.R;  // uniform: a second 16-row half
+
+    int lastkey[NH];
+    bf16x8 qf[NH][NST];
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+        const int r = rb * 32 + 16 * hb + c16;
+        const bool row_ok = r < a.R;
+        const int ti = row_ok ? r / a.g : 0;
+        const int head = kvh * a.g + (row_ok ? r % a.g : 0);
+        lastkey[hb] = row_ok ? off + ti : -1;
+        const T* row = qp + (((long long)b * a.Tq + ti) * a.Hq + head) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+            bf16x8 v{};
+            if (row_ok && (hb == 0 || two)) v = __builtin_bit_cast(bf16x8, ld16(row + 32 * s).raw);
+            qf[hb][s] = v;
+        }
+    }
+    // Keys of this chunk that any row of the block sees.
+    const int rlast = min(a.R, rb * 32 + 32) - 1;
+    const int kend_block = off + rlast / a.g + 1;
+    const int k0 = sp * a.chunk;
+    const int k1 = min(k0 + a.chunk, kend_block);
+    const int ntiles = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
+
+    // Tile loads: K rows straight into the product operand (lane = key c16 of block kb, head_dim
+    // 32 s + 8 q4 .. +7), V rows as 16-byte chunks for the LDS tile.  Rows past the chunk read
+    // as zero.
+    Vec16<T> kreg[2][NST], vreg[C::VCH];
+    const long long kv_row0 = (long long)b * a.Tk;
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int s = k0 + t * kKT + 16 * kb + c16;
+            const bool ok = s < k1;
+            const T* krow = kp + ((kv_row0 + s) * a.Hkv + kvh) * D + 8 * q4;
+#pragma unroll
+            for (int st = 0; st < NST; ++st) kreg[kb][st] = ok ? ld16(krow + 32 * st) : zero16<T>();
+        }
+#pragma unroll
+        for (int n = 0; n < C::VCH; ++n) {
+            const int u = lane + 64 * n;
+            const int key = u / C::CPR, part = u % C::CPR;
+            const int sv = k0 + t * kKT + key;
+            vreg[n] = (sv < k1) ? ld16(vp + ((kv_row0 + sv) * a.Hkv + kvh) * D + part * C::EPC) : zero16<T>();
+        }
+    };
+    auto wave_sync = [&]() {  // LDS writes of this wave visible to its later reads, and back
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto rowmax = [](float x) {
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        return fmaxf(x, __shfl_xor(x, 32, 64));
+    };
+
+    float mrun[NH], l[NH];
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+        mrun[hb] = -INFINITY;
+        l[hb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[hb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // Transposing-read addresses of V^T (keys 4 q4 + (c16 >> 2), then 16 more; head_dim
+    // 16 db + 4 (c16 & 3)).
+    const T* vt0 = Vs + (4 * q4 + (c16 >> 2)) * C::VS + 4 * (c16 & 3);
+
+    if (ntiles > 0) fetch(0);
+    for (int t = 0; t < ntiles; ++t) {
+        // Commit V of tile t to LDS; take K of tile t from the registers.
+        wave_sync();  // the previous tile's V reads are done
+#pragma unroll
+        for (int n = 0; n < C::VCH; ++n) {
+            const int u = lane + 64 * n;
+            st16(&Vs[(u / C::CPR) * C::VS + (u % C::CPR) * C::EPC], vreg[n]);
+        }
+        bf16x8 kf[2][NST];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int st = 0; st < NST; ++st) kf[kb][st] = __builtin_bit_cast(bf16x8, kreg[kb][st].raw);
+        wave_sync();
+        if (t + 1 < ntiles) fetch(t + 1);
+
+        const int kbase = k0 + t * kKT;
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb) {
+            if (hb == 1 && !two) break;
+            // S^T = K Q^T for the two 16-key blocks, masked where key > the row's last key.
+            f32x4 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < NST; ++st) sacc[kb] = mma16(kf[kb][st], qf[hb][st], sacc[kb]);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (kbase + 16 * kb + 4 * q4 + i > lastkey[hb]) sacc[kb][i] = -INFINITY;
+                    mx = fmaxf(mx, sacc[kb][i]);
+                }
+            mx = rowmax(mx) * a.sl2;
+            const float mnew = fmaxf(mrun[hb], mx);
+            const float mbase = (mnew == -INFINITY) ? 0.0f : mnew;  // rows with no key so far
+            const float alpha = __builtin_amdgcn_exp2f(mrun[hb] - mbase);
+            float rs = 0.0f;
+            bf16x8 pf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(sacc[kb][i] * a.sl2 - mbase);
+                    rs += p;
+                    pf[4 * kb + i] = (bf16)p;
+                }
+            l[hb] = l[hb] * alpha + rs;  // this lane's share of the row sum
+            mrun[hb] = mnew;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                oacc[hb][db] *= alpha;
+                const bf16x4 lo = tr4(vt0 + 16 * db);
+                const bf16x4 hi = tr4(vt0 + 16 * C::VS + 16 * db);
+                bf16x8 vf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vf[e] = lo[e];
+                    vf[4 + e] = hi[e];
+                }
+                oacc[hb][db] = mma16(vf, pf, oacc[hb][db]);
+            }
+        }
+    }
+
+    // Row totals (four lanes share a row) and the chunk's result.
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+        float lt = l[hb] + __shfl_xor(l[hb], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        lse[hb] = lt > 0.0f ? (mrun[hb] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[hb][db] *= inv;
+    }
+}
+
 // The split launch: one wave per (batch, K/V head, row block, chunk); with several chunks the
 // partials go to the workspace for decode_merge_kernel, with one chunk straight to O and LSE.
-template <typename T, int D>
+template <typename T, int D, int NH>
 __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArgs a) {
     using C = DecCfg<T, D>;
     __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * kKT * C::VS];
@@ -225,6 +421,36 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     const int kvh = (int)(rest % a.Hkv);
     const int b = (int)(rest / a.Hkv);
 
+    if constexpr (kDec16<T, D>) {
+        f32x4 o16[NH][D / 16];
+        float l16[NH];
+        decode_chunk16<D, NH>(a, Vsh + w * kKT * C::VS, b, kvh, rb, sp, o16, l16);
+        const int q4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb) {
+            const int rr = 16 * hb + c16;  // row within the block
+            const int r = rb * 32 + rr;
+            if (r >= a.R) continue;  // padding rows; the merge reads real rows only
+            if (a.nsplit == 1) {
+                const int ti = r / a.g, head = kvh * a.g + r % a.g;
+                T* orow = static_cast<T*>(a.o) + (((long long)b * a.Tq + ti) * a.Hq + head) * D;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = from_f32<T>(o16[hb][db][i]);
+                    *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * q4) = v;
+                }
+                if (q4 == 0) a.lse[((long long)b * a.Hq + head) * a.Tq + ti] = l16[hb];
+            } else {
+                float* po = a.part_o + item * 32 * D + (long long)rr * D;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * q4) = o16[hb][db];
+                if (q4 == 0) a.part_lse[item * 32 + rr] = l16[hb];
+            }
+        }
+        return;
+    }
     f32x16 oacc[C::NDB];
     float lse;
     decode_chunk<T, D>(a, Vsh + w * kKT * C::VS, b, kvh, rb, sp, oacc, lse);
@@ -264,7 +490,7 @@ constexpr int fused_max_chunks() {
     return D >= 128 ? 4 : (sizeof(T) == 2 && D <= 32) ? 16 : 8;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NH>
 __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_kernel(DecArgs a) {
     using C = DecCfg<T, D>;
     constexpr int NW = fused_max_chunks<T, D>();
@@ -287,10 +513,25 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     const int kvh = (blockIdx.x / a.nrb) % a.Hkv;
     const int b = blockIdx.x / (a.nrb * a.Hkv);
 
-    f32x16 oacc[C::NDB];
-    float lse;
-    decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, oacc, lse);
-    {
+    if constexpr (kDec16<T, D>) {
+        f32x4 o16[NH][D / 16];
+        float l16[NH];
+        decode_chunk16<D, NH>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, o16, l16);
+        const int q4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+        for (int hb = 0; hb < NH; ++hb) {
+            const int rr = 16 * hb + c16;
+            float* po = part + (size_t)w * 32 * PST + rr * PST;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) po[16 * db + 4 * q4 + i] = o16[hb][db][i];
+            if (q4 == 0) lses[w * 32 + rr] = l16[hb];
+        }
+    } else {
+        f32x16 oacc[C::NDB];
+        float lse;
+        decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, oacc, lse);
         float* po = part + (size_t)w * 32 * PST + l32 * PST;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
@@ -437,8 +678,8 @@ DecPlan plan_decode(int B, int Tq, int Tk, int Hq, int Hkv) {
     return p;
 }
 
-template <typename T, int D>
-hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
+template <typename T, int D, int NH>
+hipError_t launch_decode_nh(DecArgs a, hipStream_t stream) {
     // Caches split into at most twice as many chunks as the single launch has waves take the
     // single launch, with fewer, longer chunks: the second launch and the workspace round trip
     // cost more there than the waves the split would add.
@@ -450,13 +691,13 @@ hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
         a.nsplit = (a.Tk + a.chunk - 1) / a.chunk;
         const long long blocks = (long long)a.B * a.Hkv * a.nrb;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_fused_kernel<T, D>), dim3((unsigned)blocks), dim3(64 * a.nsplit), 0, stream, a);
+        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH>), dim3((unsigned)blocks), dim3(64 * a.nsplit), 0, stream, a);
         return hipGetLastError();
     }
     const long long items = (long long)a.B * a.Hkv * a.nrb * a.nsplit;
     const long long blocks = (items + kWavesPerWG - 1) / kWavesPerWG;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3((unsigned)blocks), dim3(64 * kWavesPerWG), 0,
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, NH>), dim3((unsigned)blocks), dim3(64 * kWavesPerWG), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
@@ -464,6 +705,16 @@ hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
     if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)rows), dim3(64), 0, stream, a);
     return hipGetLastError();
+}
+
+// bf16 at head_dim 64 and 128 runs the 16-row products; when no row block has more than 16
+// rows (R <= 16, the usual decode shapes), kernels without a second half keep fewer registers.
+template <typename T, int D>
+hipError_t launch_decode_t(DecArgs a, hipStream_t stream) {
+    if constexpr (kDec16<T, D>) {
+        if (a.R <= 16) return launch_decode_nh<T, D, 1>(a, stream);
+    }
+    return launch_decode_nh<T, D, 2>(a, stream);
 }
 
 }  // namespace

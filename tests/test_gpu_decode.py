@@ -4,6 +4,8 @@ attn_fwd_kv on the same seeded inputs, through the C ABI.
 Cases cover one and several new tokens, caches that fit one chunk (no merge), caches split
 over a few chunks (one launch, merged in LDS: B2_Tq2_Tk100, B1_Tq4_Tk129, B1_Tq16_Tk777,
 B2_Tq5_Tk2049, B1_Tq11_Tk300) and over many (merge launch: B3_Tq1_Tk1000, B4_Tq1_Tk4097),
+row blocks of more than 16 rows for the bf16 16-row products (B1_Tq6_Tk300, B2_Tq8_Tk2000,
+B1_Tq12_Tk700),
 ragged cache lengths, every head_dim, both dtypes and several head groupings; the cache shape of a 32/8-head, head_dim-128 model at
 8192 cached positions is run at full size.  With Tq = Tk the result must match attn_fwd.
 """
@@ -24,6 +26,9 @@ CASES = [  # B, Tq, Tk, Hq, Hkv, D, dtype
     (2, 2, 100, 12, 4, 64, "bf16"), (1, 4, 129, 4, 4, 128, "bf16"), (3, 1, 1000, 32, 8, 128, "bf16"),
     (1, 16, 777, 12, 4, 64, "f32"), (2, 5, 2049, 6, 2, 32, "bf16"), (1, 11, 300, 4, 1, 128, "f32"),
     (4, 1, 4097, 12, 4, 64, "bf16"),
+    # bf16 head_dim 64 / 128 run 16-row products: more than 16 rows per block (18: a partly
+    # filled second half; 32: both halves full, split launch; 36: a second row block).
+    (1, 6, 300, 12, 4, 64, "bf16"), (2, 8, 2000, 16, 4, 128, "bf16"), (1, 12, 700, 12, 4, 64, "bf16"),
 ]
 
 
