@@ -42,6 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
     "attn_fwd": ["causal_gqa_attention_fwd_amd/csrc/attn_fwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
     "attn_bwd_main": ["causal_gqa_attention_fwd_amd/csrc/attn_bwd.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
+    "attn_decode": ["causal_gqa_attention_fwd_amd/csrc/attn_decode.hip", "causal_gqa_attention_fwd_amd/csrc/ea_common.h"],
 }
 
 
@@ -167,21 +168,26 @@ def time_workload(name, steps, warmup, torch, ea, W):
     return w, step, ms, wall, kern_us
 
 
-def roofline_for(w, kern_us, name):
-    alg = algorithmic(w)[name]
-    dur_s = kern_us[name] * 1e-6
-    traffic = None
+def measured_traffic(name, workload):
+    """HBM bytes per launch of entry point `name` on `workload` from the committed counter
+    summary, or None: entries are keyed "<entry point>@<workload>" and count only while the
+    kernel sources still hash to the value recorded with them."""
     try:
         with open(TRAFFIC_FILE) as f:
             tc = json.load(f)
-        # Entries are keyed "<entry point>@<workload>"; a figure counts only while the
-        # kernel sources still hash to the value recorded with it.
-        ent = tc.get("kernels", {}).get("%s@%s" % (name, w.name))
+        ent = tc.get("kernels", {}).get("%s@%s" % (name, workload))
         if (ent and name in KERNEL_SOURCES
                 and ent.get("source_sha") == sources_sha(KERNEL_SOURCES[name])):
-            traffic = ent.get("hbm_bytes_per_launch")
+            return ent.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
-        traffic = None
+        pass
+    return None
+
+
+def roofline_for(w, kern_us, name):
+    alg = algorithmic(w)[name]
+    dur_s = kern_us[name] * 1e-6
+    traffic = measured_traffic(name, w.name)
     if "flops" in alg:
         achieved = alg["flops"] / dur_s / 1e12
         peak = PEAK_TFLOPS[w.dtype]
@@ -232,9 +238,10 @@ def time_decode(name, steps, warmup, torch, ea, W):
     gbs = w.hbm_bytes() / (us * 1e-6) / 1e9
     return {"config": w.describe(), "calls": steps, "us_per_call": round(us, 2),
             "hbm_bytes_per_call": w.hbm_bytes(),
-            "roofline": {"kernel": "attn_decode (partial + merge launches)", "bound": "hbm",
+            "roofline": {"kernel": "attn_decode (one launch, or chunk partials + merge)", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("attn_decode", name)}}
 
 
 def time_fwd_rope(name, steps, warmup, torch, ea, W):

@@ -274,27 +274,43 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
     const int k1 = min(k0 + a.chunk, kend_block);
     const int ntiles = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
 
+    // A row past the chunk's last key is masked for every row of the block (chunks are whole
+    // tiles, so a tile crosses k1 only where k1 is past the block's last row's key).
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) lastkey[hb] = min(lastkey[hb], k1 - 1);
+
     // Tile loads: K rows straight into the product operand (lane = key c16 of block kb, head_dim
-    // 32 s + 8 q4 .. +7), V rows as 16-byte chunks for the LDS tile.  Rows past the chunk read
-    // as zero.
+    // 32 s + 8 q4 .. +7), V rows as 16-byte chunks for the LDS tile.  Each lane keeps running
+    // row pointers, one tile apart per step, instead of forming every address again; a row past
+    // the chunk reads the chunk's last row instead, whose key the mask removes (P = 0 there), so
+    // no load is conditional.
     Vec16<T> kreg[2][NST], vreg[C::VCH];
-    const long long kv_row0 = (long long)b * a.Tk;
-    auto fetch = [&](int t) {
+    constexpr int VROWS = 64 / C::CPR;           // rows between a lane's successive V chunks
+    const long long rs = (long long)a.Hkv * D;  // elements from one cache row to the next
+    const long long head0 = ((long long)b * a.Tk * a.Hkv + kvh) * D;
+    const int vkey = lane / C::CPR;  // this lane's first V row within a tile
+    const T* kb0 = kp + head0 + 8 * q4;
+    const T* vb0 = vp + head0 + (lane % C::CPR) * C::EPC;
+    const long long klast = max(k1 - 1, 0);
+    const T* kcl = kb0 + klast * rs;
+    const T* vcl = vb0 + klast * rs;
+    const T* kr[2] = {kb0 + (k0 + c16) * rs, kb0 + (k0 + 16 + c16) * rs};
+    const T* vr = vb0 + (k0 + vkey) * rs;
+    auto fetch = [&](int t) {  // called once per tile, in order
+        const int lim = k1 - k0 - t * kKT;  // rows of this tile inside the chunk
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int s = k0 + t * kKT + 16 * kb + c16;
-            const bool ok = s < k1;
-            const T* krow = kp + ((kv_row0 + s) * a.Hkv + kvh) * D + 8 * q4;
+            const T* p = (16 * kb + c16 < lim) ? kr[kb] : kcl;
 #pragma unroll
-            for (int st = 0; st < NST; ++st) kreg[kb][st] = ok ? ld16(krow + 32 * st) : zero16<T>();
+            for (int st = 0; st < NST; ++st) kreg[kb][st] = ld16(p + 32 * st);
+            kr[kb] += kKT * rs;
         }
 #pragma unroll
         for (int n = 0; n < C::VCH; ++n) {
-            const int u = lane + 64 * n;
-            const int key = u / C::CPR, part = u % C::CPR;
-            const int sv = k0 + t * kKT + key;
-            vreg[n] = (sv < k1) ? ld16(vp + ((kv_row0 + sv) * a.Hkv + kvh) * D + part * C::EPC) : zero16<T>();
+            const T* p = (vkey + VROWS * n < lim) ? vr + VROWS * n * rs : vcl;
+            vreg[n] = ld16(p);
         }
+        vr += kKT * rs;
     };
     auto wave_sync = [&]() {  // LDS writes of this wave visible to its later reads, and back
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -29,6 +29,9 @@ CASES = [  # B, Tq, Tk, Hq, Hkv, D, dtype
     # bf16 head_dim 64 / 128 run 16-row products: more than 16 rows per block (18: a partly
     # filled second half; 32: both halves full, split launch; 36: a second row block).
     (1, 6, 300, 12, 4, 64, "bf16"), (2, 8, 2000, 16, 4, 128, "bf16"), (1, 12, 700, 12, 4, 64, "bf16"),
+    # Chunks of an odd number of 32-key tiles (96 keys) in the single launch (the split launch
+    # meets them at 4 x 4097 above).
+    (1, 2, 330, 12, 4, 64, "bf16"),
 ]
 
 
