@@ -141,9 +141,11 @@ ea_status attn_fwd_noncausal(const void* q, const void* k, const void* v, void* 
  * LSE_i = log sum_s exp(scale * <q_i, k_s>), with the same K/V-head map as attn_fwd.  With
  * Tq = Tk the result is attn_fwd's (attn_fwd is the faster kernel for that case).
  * Outputs: o [B, Tq, Hq, D] in dt; lse [B, Hq, Tq] float32 (natural log).
- * The cache is split into chunks read by independent waves; workspace (at least
- * attn_decode_workspace_size(...) bytes, 256-byte aligned, contents ignored) holds the
- * per-chunk partial results, merged exactly by a second launch.
+ * The cache is split into chunks read by independent waves and their partial results are
+ * merged exactly (in a fixed order: bitwise reproducible).  When a group's chunks fit one
+ * workgroup (at most 4-16 chunks by head_dim and type) one launch merges them through LDS;
+ * otherwise the partials go to the workspace (at least attn_decode_workspace_size(...)
+ * bytes, 256-byte aligned, contents ignored) and a second launch merges them.
  * Errors: as attn_fwd (with T = Tk), plus Tq < 1 or Tq > Tk (EA_ERR_INVALID_ARG), workspace
  * too small (EA_ERR_WORKSPACE) or not 256-byte aligned (EA_ERR_ALIGN), and o, lse or the
  * workspace overlapping an input or each other (EA_ERR_ALIAS).
