@@ -284,34 +284,28 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
     // row pointers, one tile apart per step, instead of forming every address again; a row past
     // the chunk reads the chunk's last row instead, whose key the mask removes (P = 0 there), so
     // no load is conditional.
-    Vec16<T> kreg[2][NST], vreg[C::VCH];
-    constexpr int VROWS = 64 / C::CPR;           // rows between a lane's successive V chunks
+    Vec16<T> kreg[C::VCH], vreg[C::VCH];
+    constexpr int VROWS = 64 / C::CPR;           // rows between a lane's successive chunks
     const long long rs = (long long)a.Hkv * D;  // elements from one cache row to the next
-    const long long head0 = ((long long)b * a.Tk * a.Hkv + kvh) * D;
-    const int vkey = lane / C::CPR;  // this lane's first V row within a tile
-    const T* kb0 = kp + head0 + 8 * q4;
-    const T* vb0 = vp + head0 + (lane % C::CPR) * C::EPC;
+    const long long head0 = ((long long)b * a.Tk * a.Hkv + kvh) * D + (lane % C::CPR) * C::EPC;
+    const int vkey = lane / C::CPR;  // this lane's first row within a tile
     const long long klast = max(k1 - 1, 0);
-    const T* kcl = kb0 + klast * rs;
-    const T* vcl = vb0 + klast * rs;
-    const T* kr[2] = {kb0 + (k0 + c16) * rs, kb0 + (k0 + 16 + c16) * rs};
-    const T* vr = vb0 + (k0 + vkey) * rs;
+    const T* kcl = kp + head0 + klast * rs;
+    const T* vcl = vp + head0 + klast * rs;
+    const T* kr = kp + head0 + (k0 + vkey) * rs;
+    const T* vr = vp + head0 + (k0 + vkey) * rs;
     auto fetch = [&](int t) {  // called once per tile, in order
         const int lim = k1 - k0 - t * kKT;  // rows of this tile inside the chunk
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const T* p = (16 * kb + c16 < lim) ? kr[kb] : kcl;
-#pragma unroll
-            for (int st = 0; st < NST; ++st) kreg[kb][st] = ld16(p + 32 * st);
-            kr[kb] += kKT * rs;
-        }
-#pragma unroll
         for (int n = 0; n < C::VCH; ++n) {
-            const T* p = (vkey + VROWS * n < lim) ? vr + VROWS * n * rs : vcl;
-            vreg[n] = ld16(p);
+            const bool in = vkey + VROWS * n < lim;
+            kreg[n] = ld16(in ? kr + VROWS * n * rs : kcl);
+            vreg[n] = ld16(in ? vr + VROWS * n * rs : vcl);
         }
+        kr += kKT * rs;
         vr += kKT * rs;
     };
+    T* const Ks = Vs + kKT * C::VS;  // the K tile, after the V tile
     auto wave_sync = [&]() {  // LDS writes of this wave visible to its later reads, and back
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -343,13 +337,15 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
         for (int n = 0; n < C::VCH; ++n) {
             const int u = lane + 64 * n;
             st16(&Vs[(u / C::CPR) * C::VS + (u % C::CPR) * C::EPC], vreg[n]);
+            st16(&Ks[(u / C::CPR) * C::VS + (u % C::CPR) * C::EPC], kreg[n]);
         }
+        wave_sync();
         bf16x8 kf[2][NST];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int st = 0; st < NST; ++st) kf[kb][st] = __builtin_bit_cast(bf16x8, kreg[kb][st].raw);
-        wave_sync();
+            for (int st = 0; st < NST; ++st)
+                kf[kb][st] = __builtin_bit_cast(bf16x8, ld16(&Ks[(16 * kb + c16) * C::VS + 32 * st + 8 * q4]).raw);
         if (t + 1 < ntiles) fetch(t + 1);
 
         const int kbase = k0 + t * kKT;
@@ -421,7 +417,8 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
 template <typename T, int D, int NH>
 __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArgs a) {
     using C = DecCfg<T, D>;
-    __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * kKT * C::VS];
+    constexpr int VT = kDec16<T, D> ? 2 * kKT : kKT;  // rows staged per wave (K too on the 16-row path)
+    __shared__ __attribute__((aligned(16))) T Vsh[kWavesPerWG * VT * C::VS];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -440,7 +437,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     if constexpr (kDec16<T, D>) {
         f32x4 o16[NH][D / 16];
         float l16[NH];
-        decode_chunk16<D, NH>(a, Vsh + w * kKT * C::VS, b, kvh, rb, sp, o16, l16);
+        decode_chunk16<D, NH>(a, Vsh + w * VT * C::VS, b, kvh, rb, sp, o16, l16);
         const int q4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
         for (int hb = 0; hb < NH; ++hb) {
@@ -469,7 +466,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_partial_kernel(DecArg
     }
     f32x16 oacc[C::NDB];
     float lse;
-    decode_chunk<T, D>(a, Vsh + w * kKT * C::VS, b, kvh, rb, sp, oacc, lse);
+    decode_chunk<T, D>(a, Vsh + w * VT * C::VS, b, kvh, rb, sp, oacc, lse);
 
     const int r = rb * 32 + l32;
     if (r >= a.R) return;  // padding rows; the merge reads real rows only
@@ -511,7 +508,8 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     using C = DecCfg<T, D>;
     constexpr int NW = fused_max_chunks<T, D>();
     constexpr int PST = D + 1;  // row stride of a partial (odd: lanes of one column on distinct banks)
-    constexpr size_t V_BYTES = (size_t)NW * kKT * C::VS * sizeof(T);
+    constexpr int VT = kDec16<T, D> ? 2 * kKT : kKT;  // rows staged per wave (K too on the 16-row path)
+    constexpr size_t V_BYTES = (size_t)NW * VT * C::VS * sizeof(T);
     constexpr size_t P_BYTES = (size_t)NW * 32 * PST * sizeof(float);
     static_assert(V_BYTES % 16 == 0 && V_BYTES + P_BYTES + 2 * NW * 32 * sizeof(float) <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char smem[V_BYTES + P_BYTES + 2 * NW * 32 * sizeof(float)];
@@ -532,7 +530,7 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     if constexpr (kDec16<T, D>) {
         f32x4 o16[NH][D / 16];
         float l16[NH];
-        decode_chunk16<D, NH>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, o16, l16);
+        decode_chunk16<D, NH>(a, reinterpret_cast<T*>(smem) + w * VT * C::VS, b, kvh, rb, w, o16, l16);
         const int q4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
         for (int hb = 0; hb < NH; ++hb) {
@@ -547,7 +545,7 @@ __global__ __launch_bounds__((64 * fused_max_chunks<T, D>())) void decode_fused_
     } else {
         f32x16 oacc[C::NDB];
         float lse;
-        decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * kKT * C::VS, b, kvh, rb, w, oacc, lse);
+        decode_chunk<T, D>(a, reinterpret_cast<T*>(smem) + w * VT * C::VS, b, kvh, rb, w, oacc, lse);
         float* po = part + (size_t)w * 32 * PST + l32 * PST;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
