@@ -279,9 +279,11 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) lastkey[hb] = min(lastkey[hb], k1 - 1);
 
-    // Tile loads: K rows straight into the product operand (lane = key c16 of block kb, head_dim
-    // 32 s + 8 q4 .. +7), V rows as 16-byte chunks for the LDS tile.  Each lane keeps running
-    // row pointers, one tile apart per step, instead of forming every address again; a row past
+    // Tile loads: K and V rows as 16-byte chunks for the wave's LDS tiles, consecutive lanes on
+    // consecutive chunks of a row, so that each load instruction covers whole rows (loading K
+    // straight into the product operand would take sixteen half rows per instruction, and the
+    // CU's load path, not HBM, bounds the small-batch cases).  Each lane keeps running row
+    // pointers, one tile apart per step, instead of forming every address again; a row past
     // the chunk reads the chunk's last row instead, whose key the mask removes (P = 0 there), so
     // no load is conditional.
     Vec16<T> kreg[C::VCH], vreg[C::VCH];
@@ -331,8 +333,9 @@ __device__ __forceinline__ void decode_chunk16(const DecArgs& a, bf16* Vs, int b
 
     if (ntiles > 0) fetch(0);
     for (int t = 0; t < ntiles; ++t) {
-        // Commit V of tile t to LDS; take K of tile t from the registers.
-        wave_sync();  // the previous tile's V reads are done
+        // Commit K and V of tile t to LDS, then read K's operand fragments back (lane = key c16
+        // of block kb, head_dim 32 s + 8 q4 .. +7).
+        wave_sync();  // the previous tile's K and V reads are done
 #pragma unroll
         for (int n = 0; n < C::VCH; ++n) {
             const int u = lane + 64 * n;
