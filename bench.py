@@ -288,7 +288,7 @@ def time_fwd_rope(name, steps, warmup, torch, ea, W):
         torch.cuda.synchronize()
         res[label] = round(1000.0 * t0.elapsed_time(t1) / steps, 2)
     return {"config": w.describe(), "calls": steps, **res,
-            "note": "two launches either way; the headline step keeps rope_apply_qk + attn_fwd"}
+            "note": "two launches either way (attn_fwd_rope rotates Q with K in its first launch where attn_fwd_rope_fuses_q is 0); the steps keep rope_apply_qk + attn_fwd, since inside the whole step the two forms measured the same"}
 
 
 def time_noncausal(name, steps, warmup, torch, ea, W):

@@ -30,7 +30,7 @@ import os
 import torch
 
 __all__ = ["rope_apply", "rope_apply_qk", "attn_fwd", "attn_fwd_noncausal", "attn_fwd_rope",
-           "attn_fwd_rope_workspace_size", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
+           "attn_fwd_rope_workspace_size", "attn_fwd_rope_fuses_q", "attn_bwd", "attn_bwd_noncausal", "attn_bwd_workspace_size", "attn_bwd_preprocess",
            "attn_bwd_main", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_rope", "attn_bwd_rope_workspace_size",
            "attn_bwd_rope_preprocess", "attn_bwd_rope_main", "attn_decode", "attn_decode_workspace_size", "gemm",
            "qkv_proj", "qkv_proj_bwd", "gemm_workspace_size", "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH", "EA_F32",
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_noncausal.restype = ci
     L.attn_fwd_rope_workspace_size.argtypes = [ci, ci]
     L.attn_fwd_rope_workspace_size.restype = sz
+    L.attn_fwd_rope_fuses_q.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_fwd_rope_fuses_q.restype = ci
     L.attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, cd, ci, vp]
     L.attn_fwd_rope.restype = ci
     L.attn_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -217,6 +219,13 @@ def attn_fwd_noncausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale:
 def attn_fwd_rope_workspace_size(T: int, D: int) -> int:
     """Bytes of the workspace attn_fwd_rope needs (the RoPE (cos, sin) table)."""
     return int(lib().attn_fwd_rope_workspace_size(T, D))
+
+
+def attn_fwd_rope_fuses_q(B: int, T: int, Hq: int, Hkv: int, D: int, dtype=torch.bfloat16) -> int:
+    """1 if attn_fwd_rope rotates the queries inside the forward at this shape, 0 if its first
+    launch rotates them with K, -1 for sizes attn_fwd rejects (host-only query)."""
+    code = EA_F32 if dtype == torch.float32 else EA_BF16
+    return int(lib().attn_fwd_rope_fuses_q(B, T, Hq, Hkv, D, code))
 
 
 def attn_fwd_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, base: float = 10000.0,

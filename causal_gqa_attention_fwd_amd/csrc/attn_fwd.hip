@@ -591,6 +591,25 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool fwd_splits_keys(int B, int T, int Hq, int Hkv, int D, IoType dt) {
+    FwdArgs a{};
+    a.B = B;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    int G, WPH, KSPL;
+    if (dt == kF32) {
+        if (D == 32) pick_fwd_shape<float, 32>(a, &G, &WPH, &KSPL);
+        else if (D == 64) pick_fwd_shape<float, 64>(a, &G, &WPH, &KSPL);
+        else pick_fwd_shape<float, 128>(a, &G, &WPH, &KSPL);
+    } else {
+        if (D == 32) pick_fwd_shape<bf16, 32>(a, &G, &WPH, &KSPL);
+        else if (D == 64) pick_fwd_shape<bf16, 64>(a, &G, &WPH, &KSPL);
+        else pick_fwd_shape<bf16, 128>(a, &G, &WPH, &KSPL);
+    }
+    return KSPL > 1;
+}
+
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int Hq, int Hkv, int D, float scale, IoType dt,
                            bool causal, hipStream_t stream, const float* qtab, void* q_r) {

@@ -28,6 +28,9 @@ hipError_t launch_rope_pair(const void* x0, void* y0, int H0, const void* x1, vo
                             int B, int T, int D, IoType dt, double base, int pos0, int inverse,
                             hipStream_t stream);
 
+// Whether attn_fwd splits each query block's keys over two waves at this shape (small
+// problems); D in {32, 64, 128}.
+bool fwd_splits_keys(int B, int T, int Hq, int Hkv, int D, IoType dt);
 // Forward: o [B, T, Hq, D], lse [B, Hq, T] (natural log); causal = false lets every query
 // see every key.
 // With qtab set, q holds the pre-RoPE queries: each row is rotated by the (cos, sin) table

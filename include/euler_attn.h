@@ -102,10 +102,14 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * launches on stream: K is rotated once (into k_r), which also fills the (cos, sin) table of
  * every (position, pair) in the workspace; the forward then rotates each query row as it
  * loads it (queries stay in registers for the whole key loop, so each is rotated once) and
- * writes it to q_r.  Outputs: o, lse as attn_fwd; q_r, k_r the rotated q and k in dt, the
- * inputs attn_bwd / attn_bwd_rope need.  Angles and arithmetic are rope_apply's (base, pos0,
- * adjacent pairs; float64 angle reduction, float32 rotation); k_r equals rope_apply's output
- * bitwise.
+ * writes it to q_r.  Where that does not pay (attn_fwd_rope_fuses_q returns 0: sequences
+ * shorter than 2048 positions, whose query tiles have too few key tiles to hide the rotation,
+ * and problems whose forward splits each query block's keys over two waves) the first launch
+ * rotates Q and K together instead and the forward reads q_r; the outputs are bitwise the
+ * same either way.  Outputs: o, lse as attn_fwd; q_r, k_r the rotated q and k in dt, the inputs
+ * attn_bwd / attn_bwd_rope need.  Angles and arithmetic are rope_apply's (base, pos0,
+ * adjacent pairs; float64 angle reduction, float32 rotation); q_r and k_r equal rope_apply's
+ * output bitwise.
  * workspace: at least attn_fwd_rope_workspace_size(T, D) bytes, 16-byte aligned, contents on
  * entry don't care (attn_fwd_rope_workspace_size returns 0 for T < 1 or D odd or < 2).
  * Errors: as attn_fwd, plus NULL q_r, k_r or workspace (EA_ERR_NULL); base <= 1 or not finite,
@@ -114,6 +118,10 @@ ea_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * input here, in-place rotation included).
  */
 size_t attn_fwd_rope_workspace_size(int T, int D);
+/* attn_fwd_rope_fuses_q -- 1 if attn_fwd_rope rotates the queries inside the forward at this
+ * shape, 0 if its first launch rotates them with K instead, -1 for sizes attn_fwd rejects.
+ * Host-only: launches nothing. */
+int attn_fwd_rope_fuses_q(int B, int T, int Hq, int Hkv, int D, ea_dtype dt);
 ea_status attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
                         void* q_r, void* k_r, void* workspace, size_t workspace_bytes, int B,
                         int T, int Hq, int Hkv, int D, float scale, ea_dtype dt, double base,

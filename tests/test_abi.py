@@ -249,6 +249,20 @@ def test_fwd_rope_workspace_and_validation(L):
     assert fr(kr=fake(5)) == ALIAS        # q_r and k_r overlap
 
 
+def test_fwd_rope_fuses_q(L):
+    # Host-only: the queries are rotated inside the forward for sequences of 2048 positions or
+    # more, except where the forward splits each query block's keys over two waves (bf16,
+    # head_dim <= 64, at most 2048 blocks of 32 query rows).
+    assert L.attn_fwd_rope_fuses_q(4, 1024, 12, 4, 64, BF16) == 0     # short
+    assert L.attn_fwd_rope_fuses_q(16, 512, 12, 4, 64, BF16) == 0     # short
+    assert L.attn_fwd_rope_fuses_q(2, 8192, 12, 4, 64, BF16) == 1     # 6144 blocks: no split
+    assert L.attn_fwd_rope_fuses_q(8, 4096, 32, 8, 128, BF16) == 1    # head_dim 128: no split
+    assert L.attn_fwd_rope_fuses_q(1, 2048, 12, 4, 64, BF16) == 0     # 768 blocks: key split
+    assert L.attn_fwd_rope_fuses_q(1, 2048, 12, 4, 64, 0) == 1        # fp32: no split
+    assert L.attn_fwd_rope_fuses_q(1, 64, 3, 2, 64, BF16) == -1       # Hq not a multiple of Hkv
+    assert L.attn_fwd_rope_fuses_q(1, 64, 4, 2, 96, BF16) == -1       # unsupported head_dim
+
+
 def test_decode_workspace_and_validation(L):
     ws = L.attn_decode_workspace_size(8, 1, 8192, 32, 8, 128, BF16)
     assert ws >= 256 and ws % 256 == 0
